@@ -1,0 +1,176 @@
+"""CPU oracle for the Mixtral sparse mixture-of-experts layer (ctypes wrapper of oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline use it; the product path never does. It shares no code with the HIP
+library and does not import it. Inputs are numpy arrays: ``float32`` for fp32
+storage and ``uint16`` for bf16 bit patterns. Results are float64.
+
+Every function follows the definitions of "Mixtral of Experts" (arXiv
+2401.04088) as restated on the blog.csdn.net page (sections 1 and 2.1-2.4:
+logits x.W_g, TopK with -inf, softmax over the kept logits, gate-weighted sum)
+and the xyznot.com summary ("Método": n=8 SwiGLU experts, K=2). See oracle.cpp
+for the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-pthread", "-fPIC", "-shared", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        L.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_permute.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_gather.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32]
+        L.oracle_combine.argtypes = [i64, vp, i32, i32, vp, vp, vp, vp]
+        L.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
+                                     vp, i32]
+        L.oracle_rmsnorm_bf16.argtypes = [i64, i32, dbl, vp, vp, vp]
+        L.oracle_deep_layer.argtypes = [i64, i32, i32, i32, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        _lib = L
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"storage dtype must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+
+
+def route(x, w_gate, K, bias=None, threads=0):
+    """Returns (logits [T][E] (fp32-rounded, as float64), topk_idx [T][K] int32, topk_w [T][K] float64)."""
+    x, w_gate = _c(x), _c(w_gate)
+    bias = _c(bias, np.float32)
+    T, d = x.shape
+    E = w_gate.shape[1]
+    dt = _dtype_code(x)
+    assert _dtype_code(w_gate) == dt and w_gate.shape[0] == d
+    logits = np.empty((T, E), np.float64)
+    idx = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    lib().oracle_route(T, d, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(logits), _p(idx), _p(w), threads)
+    return logits, idx, w
+
+
+def permute(topk_idx, E):
+    """Returns (counts [E], offsets [E+1], row_token [T*K], token_row [T][K]), all int32."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, K = topk_idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    row_token = np.empty(T * K, np.int32)
+    token_row = np.empty((T, K), np.int32)
+    lib().oracle_permute(T, E, K, _p(topk_idx), _p(counts), _p(offsets), _p(row_token), _p(token_row))
+    return counts, offsets, row_token, token_row
+
+
+def gather(x, row_token):
+    x = _c(x)
+    row_token = _c(row_token, np.int32)
+    out = np.empty((row_token.shape[0], x.shape[1]), x.dtype)
+    lib().oracle_gather(row_token.shape[0], x.shape[1] * x.itemsize, _p(x), _p(row_token), _p(out))
+    return out
+
+
+def expert_ffn(x_perm, offsets, w1, w3, w2, rows=None, want_hidden=False, threads=0):
+    """y rows [n_sel][d] (float64) of the expert FFN over expert-contiguous rows."""
+    x_perm, w1, w3, w2 = _c(x_perm), _c(w1), _c(w3), _c(w2)
+    offsets = _c(offsets, np.int32)
+    dt = _dtype_code(x_perm)
+    E, F, d = w1.shape
+    assert w3.shape == (E, F, d) and w2.shape == (E, d, F) and x_perm.shape[1] == d
+    rows = np.arange(x_perm.shape[0], dtype=np.int64) if rows is None else _c(rows, np.int64)
+    y = np.empty((rows.shape[0], d), np.float64)
+    h = np.empty((rows.shape[0], F), np.float64) if want_hidden else None
+    lib().oracle_expert_ffn(d, F, E, dt, _p(x_perm), _p(offsets), _p(w1), _p(w3), _p(w2), rows.shape[0],
+                            _p(rows), _p(h), _p(y), threads)
+    return (y, h) if want_hidden else y
+
+
+def combine(y_perm, token_row, topk_w, tokens=None):
+    y_perm = _c(y_perm, np.float32)
+    token_row = _c(token_row, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, K = token_row.shape
+    d = y_perm.shape[1]
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    y = np.empty((tokens.shape[0], d), np.float64)
+    lib().oracle_combine(tokens.shape[0], _p(tokens), d, K, _p(y_perm), _p(token_row), _p(topk_w), _p(y))
+    return y
+
+
+def forward(x, w_gate, w1, w3, w2, K, bias=None, tokens=None, threads=0):
+    """Full layer on selected tokens. Returns dict(y, logits, idx, w) for those tokens."""
+    x, w_gate, w1, w3, w2 = _c(x), _c(w_gate), _c(w1), _c(w3), _c(w2)
+    bias = _c(bias, np.float32)
+    T, d = x.shape
+    E, F, _ = w1.shape
+    dt = _dtype_code(x)
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    n = tokens.shape[0]
+    y = np.empty((n, d), np.float64)
+    logits = np.empty((n, E), np.float64)
+    idx = np.empty((n, K), np.int32)
+    w = np.empty((n, K), np.float64)
+    lib().oracle_forward(T, d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n, _p(tokens),
+                         _p(y), _p(logits), _p(idx), _p(w), threads)
+    return {"y": y, "logits": logits, "idx": idx, "w": w}
+
+
+def rmsnorm_bf16(h, eps, want_exact=False):
+    h = _c(h, np.float64)
+    T, d = h.shape
+    out = np.empty((T, d), np.uint16)
+    ex = np.empty((T, d), np.float64) if want_exact else None
+    lib().oracle_rmsnorm_bf16(T, d, float(eps), _p(h), _p(out), _p(ex))
+    return (out, ex) if want_exact else out
+
+
+def deep_layer(h, w_gate, w1, w3, w2, K, eps, bias=None, threads=0):
+    """In place on h [n][d] float64: h <- h + MoE(bf16(rmsnorm(h))). Returns (idx, logits)."""
+    assert h.dtype == np.float64 and h.flags.c_contiguous
+    w_gate, w1, w3, w2 = _c(w_gate), _c(w1), _c(w3), _c(w2)
+    bias = _c(bias, np.float32)
+    n, d = h.shape
+    E, F, _ = w1.shape
+    idx = np.empty((n, K), np.int32)
+    logits = np.empty((n, E), np.float64)
+    lib().oracle_deep_layer(n, d, F, E, K, float(eps), _p(h), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2),
+                            _p(idx), _p(logits), threads)
+    return idx, logits

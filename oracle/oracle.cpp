@@ -1,0 +1,254 @@
+/*
+ * CPU oracle for the sparse mixture-of-experts layer of Mixtral 8x7B.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may call, link or load
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no code, header or table with the HIP library.
+ *
+ * It is the plain definition written out, in double precision, one token at a
+ * time, with loops a reader can check against the pages by eye:
+ *
+ *   logits      l = x . W_g, W_g in R^{d x n}                ("Mixtral of Experts"
+ *               blog on blog.csdn.net, section 2.1; xyznot.com summary, "Método")
+ *   TopK        keep the K largest logits, the others become -inf
+ *               (csdn blog section 2.2; xyznot.com "Método"; K = 2)
+ *   Softmax     over the kept logits, so the K weights sum to 1 and the
+ *               others are exactly 0 (csdn blog sections 2.3 and 2.4, with the
+ *               worked form for two selected experts)
+ *   Output      y = sum_i G(x)_i * E_i(x) (csdn blog section 1; xyznot.com
+ *               "Método"); only the K selected experts are evaluated, because
+ *               an expert with gate 0 adds nothing (ja.news.hada.io summary)
+ *   Expert      SwiGLU feed-forward block with hidden size 14336
+ *               (xyznot.com "Método" and "Términos clave": Swish times an
+ *               elementwise product), read as w2 . (silu(w1 . x) * (w3 . x)),
+ *               silu(z) = z / (1 + exp(-z)), no biases.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - ties in TopK go to the lower expert index; slot 0 holds the larger logit;
+ *   - the TopK decision is taken on logits rounded to fp32, the precision the
+ *     GPU kernel decides in; the sums themselves are exact-order double;
+ *   - rows of one expert group are ordered by ascending token index;
+ *   - the deep-stack layer is h <- h + MoE(bf16(h / sqrt(mean(h^2) + eps)))
+ *     with a unit norm weight (the pages do not describe a norm).
+ *
+ * Storage types of inputs: dtype 0 = fp32, dtype 1 = bf16 bit patterns. A bf16
+ * value is widened exactly (its 16 bits become the top half of an fp32).
+ */
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+#include <algorithm>
+
+namespace {
+
+double load(const void* p, int dtype, int64_t i) {
+  if (dtype == 0) return (double)static_cast<const float*>(p)[i];
+  uint32_t bits = (uint32_t)static_cast<const uint16_t*>(p)[i] << 16;
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+uint16_t round_to_bf16(double v) {
+  // double -> fp32 (round to nearest even) -> bf16 (round to nearest even)
+  float f = (float)v;
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if (std::isnan(f)) return 0x7FC0;
+  uint32_t rounding = 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)((u + rounding) >> 16);
+}
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+int pick_threads(int threads) {
+  if (threads > 0) return threads;
+  unsigned h = std::thread::hardware_concurrency();
+  return h ? (int)h : 1;
+}
+
+// Runs body(i) for i in [0, n) on `threads` workers, each taking a contiguous block.
+template <class F>
+void parallel_for(int64_t n, int threads, F body) {
+  int nt = (int)std::min<int64_t>(pick_threads(threads), std::max<int64_t>(n, 1));
+  if (nt <= 1) {
+    for (int64_t i = 0; i < n; ++i) body(i);
+    return;
+  }
+  std::vector<std::thread> pool;
+  for (int w = 0; w < nt; ++w) {
+    int64_t lo = n * w / nt, hi = n * (w + 1) / nt;
+    pool.emplace_back([=, &body]() { for (int64_t i = lo; i < hi; ++i) body(i); });
+  }
+  for (auto& t : pool) t.join();
+}
+
+// Router for one token: logits (fp32-rounded), TopK by repeated argmax, softmax of the kept ones.
+void route_token(int d, int E, int K, int dtype, const void* x, int64_t t, const void* w_gate,
+                 const float* bias, double* logits, int32_t* idx, double* w) {
+  for (int e = 0; e < E; ++e) {
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) s += load(x, dtype, t * d + k) * load(w_gate, dtype, (int64_t)k * E + e);
+    if (bias) s += (double)bias[e];
+    logits[e] = (double)(float)s;
+  }
+  std::vector<char> taken(E, 0);
+  for (int j = 0; j < K; ++j) {
+    int best = -1;
+    for (int e = 0; e < E; ++e)
+      if (!taken[e] && (best < 0 || logits[e] > logits[best])) best = e;
+    taken[best] = 1;
+    idx[j] = best;
+  }
+  // Softmax over TopK(l): entries set to -inf contribute exp(-inf) = 0, so only the kept ones remain.
+  double m = logits[idx[0]];
+  double z = 0.0;
+  for (int j = 0; j < K; ++j) z += std::exp(logits[idx[j]] - m);
+  for (int j = 0; j < K; ++j) w[j] = std::exp(logits[idx[j]] - m) / z;
+}
+
+// One expert applied to one d-vector: out = w2[e] . (silu(w1[e] . v) * (w3[e] . v)).
+void expert_apply(int d, int F, int e, int dtype, const void* v, int64_t v_off, int v_dtype,
+                  const void* w1, const void* w3, const void* w2, double* hid, double* out) {
+  const int64_t base13 = (int64_t)e * F * d;
+  for (int f = 0; f < F; ++f) {
+    double a = 0.0, b = 0.0;
+    for (int k = 0; k < d; ++k) {
+      double xv = load(v, v_dtype, v_off + k);
+      a += load(w1, dtype, base13 + (int64_t)f * d + k) * xv;
+      b += load(w3, dtype, base13 + (int64_t)f * d + k) * xv;
+    }
+    hid[f] = silu(a) * b;
+  }
+  const int64_t base2 = (int64_t)e * d * F;
+  for (int n = 0; n < d; ++n) {
+    double s = 0.0;
+    for (int f = 0; f < F; ++f) s += load(w2, dtype, base2 + (int64_t)n * F + f) * hid[f];
+    out[n] = s;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_abi_version() { return 1; }
+
+// logits [T][E] (double holding fp32-rounded values), topk_idx [T][K], topk_w [T][K].
+void oracle_route(int64_t T, int d, int E, int K, int dtype, const void* x, const void* w_gate,
+                  const float* bias, double* logits, int32_t* topk_idx, double* topk_w, int threads) {
+  parallel_for(T, threads, [&](int64_t t) {
+    route_token(d, E, K, dtype, x, t, w_gate, bias, logits + t * E, topk_idx + t * K, topk_w + t * K);
+  });
+}
+
+// Per-expert counts, exclusive-scan offsets [E+1], and the stable expert-contiguous order:
+// row_token[row] = token, token_row[t*K + k] = row. Rows of one expert follow ascending token index.
+void oracle_permute(int64_t T, int E, int K, const int32_t* topk_idx, int32_t* counts,
+                    int32_t* offsets, int32_t* row_token, int32_t* token_row) {
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t s = 0; s < T * K; ++s) counts[topk_idx[s]] += 1;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  std::vector<int32_t> next(offsets, offsets + E);
+  for (int64_t t = 0; t < T; ++t)
+    for (int k = 0; k < K; ++k) {
+      int e = topk_idx[t * K + k];
+      int32_t row = next[e]++;
+      row_token[row] = (int32_t)t;
+      token_row[t * K + k] = row;
+    }
+}
+
+// x_perm[row] = x[row_token[row]] (byte copy of whole rows).
+void oracle_gather(int64_t rows, int64_t row_bytes, const void* x, const int32_t* row_token, void* x_perm) {
+  for (int64_t r = 0; r < rows; ++r)
+    std::memcpy((char*)x_perm + r * row_bytes, (const char*)x + (int64_t)row_token[r] * row_bytes, row_bytes);
+}
+
+// Expert FFN over expert-contiguous rows: for the selected rows, y_sel[i] = Expert_e(x_perm[rows_sel[i]])
+// with e the group that holds that row. h_sel (nullable) receives the hidden vector [n_sel][F].
+void oracle_expert_ffn(int d, int F, int E, int dtype, const void* x_perm, const int32_t* offsets,
+                       const void* w1, const void* w3, const void* w2, int64_t n_sel,
+                       const int64_t* rows_sel, double* h_sel, double* y_sel, int threads) {
+  parallel_for(n_sel, threads, [&](int64_t i) {
+    int64_t r = rows_sel[i];
+    int e = 0;
+    while (e < E - 1 && r >= offsets[e + 1]) ++e;
+    std::vector<double> hid(F);
+    expert_apply(d, F, e, dtype, x_perm, r * d, dtype, w1, w3, w2, hid.data(), y_sel + i * d);
+    if (h_sel) std::copy(hid.begin(), hid.end(), h_sel + i * F);
+  });
+}
+
+// y[t] = sum_k topk_w[t][k] * y_perm[token_row[t][k]] for the selected tokens, slot order.
+void oracle_combine(int64_t n_sel, const int64_t* tok_sel, int d, int K, const float* y_perm,
+                    const int32_t* token_row, const float* topk_w, double* y) {
+  for (int64_t i = 0; i < n_sel; ++i) {
+    int64_t t = tok_sel[i];
+    for (int n = 0; n < d; ++n) {
+      double s = 0.0;
+      for (int k = 0; k < K; ++k)
+        s += (double)topk_w[t * K + k] * (double)y_perm[(int64_t)token_row[t * K + k] * d + n];
+      y[i * d + n] = s;
+    }
+  }
+}
+
+// Whole layer for selected tokens (tokens are independent): y_sel [n_sel][d];
+// also returns each selected token's logits [n_sel][E], topk_idx [n_sel][K], topk_w [n_sel][K].
+void oracle_forward(int64_t T, int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
+                    const float* bias, const void* w1, const void* w3, const void* w2, int64_t n_sel,
+                    const int64_t* tok_sel, double* y_sel, double* logits_sel, int32_t* idx_sel,
+                    double* w_sel, int threads) {
+  (void)T;
+  for (int64_t i = 0; i < n_sel; ++i)
+    route_token(d, E, K, dtype, x, tok_sel[i], w_gate, bias, logits_sel + i * E, idx_sel + i * K, w_sel + i * K);
+  std::vector<double> outs((size_t)n_sel * K * d);
+  parallel_for(n_sel * K, threads, [&](int64_t u) {
+    int64_t i = u / K;
+    int k = (int)(u % K);
+    std::vector<double> hid(F);
+    expert_apply(d, F, idx_sel[i * K + k], dtype, x, tok_sel[i] * d, dtype, w1, w3, w2, hid.data(),
+                 outs.data() + (size_t)u * d);
+  });
+  for (int64_t i = 0; i < n_sel; ++i)
+    for (int n = 0; n < d; ++n) {
+      double s = 0.0;
+      for (int k = 0; k < K; ++k) s += w_sel[i * K + k] * outs[((size_t)i * K + k) * d + n];
+      y_sel[i * d + n] = s;
+    }
+}
+
+// x = bf16(h / sqrt(mean(h^2) + eps)) per row (unit norm weight). x_exact (nullable) gets the unrounded value.
+void oracle_rmsnorm_bf16(int64_t T, int d, double eps, const double* h, uint16_t* x_bf16, double* x_exact) {
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int k = 0; k < d; ++k) ss += h[t * d + k] * h[t * d + k];
+    double inv = 1.0 / std::sqrt(ss / d + eps);
+    for (int k = 0; k < d; ++k) {
+      double v = h[t * d + k] * inv;
+      if (x_exact) x_exact[t * d + k] = v;
+      x_bf16[t * d + k] = round_to_bf16(v);
+    }
+  }
+}
+
+// One deep-stack layer on n rows of the residual stream (double, in place):
+// x = bf16(rmsnorm(h)); h <- h + MoE(x). idx_out [n][K] and logits_out [n][E] report the routing.
+void oracle_deep_layer(int64_t n, int d, int F, int E, int K, double eps, double* h, const void* w_gate,
+                       const float* bias, const void* w1, const void* w3, const void* w2,
+                       int32_t* idx_out, double* logits_out, int threads) {
+  std::vector<uint16_t> x((size_t)n * d);
+  oracle_rmsnorm_bf16(n, d, eps, h, x.data(), nullptr);
+  std::vector<int64_t> sel(n);
+  for (int64_t i = 0; i < n; ++i) sel[i] = i;
+  std::vector<double> y((size_t)n * d), w((size_t)n * K);
+  oracle_forward(n, d, F, E, K, 1, x.data(), w_gate, bias, w1, w3, w2, n, sel.data(), y.data(), logits_out,
+                 idx_out, w.data(), threads);
+  for (size_t i = 0; i < (size_t)n * d; ++i) h[i] += y[i];
+}
+
+}  // extern "C"
