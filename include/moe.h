@@ -1,0 +1,159 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse mixture-of-experts layer library.
+ *
+ * The layer is the one of "Mixtral of Experts" (arXiv 2401.04088):
+ *
+ *     G(x) = Softmax(TopK(x . W_g)),     y = sum_i G(x)_i * SwiGLU_i(x)
+ *
+ * with n = E experts, K of them kept per token (Mixtral: E = 8, K = 2), and each
+ * expert SwiGLU_i(x) = w2_i . (silu(w1_i . x) * (w3_i . x)). The gating formula
+ * and the output sum are those of the xyznot.com summary ("Método") and of the
+ * blog.csdn.net explainer (sections 1 and 2.1-2.4); SwiGLU with hidden size
+ * 14336 on d = 4096 comes from the same summary. Experts whose gate is 0 are
+ * not evaluated (ja.news.hada.io summary), and the number of tokens per expert
+ * varies from call to call (zh.newsflash.city article, section on the
+ * mixture-of-experts layer), which is why the calls below group tokens by
+ * expert before the expert matmuls and return them to token order afterwards.
+ *
+ * The five calls mirror the stages of the layer one to one:
+ *     moe_route       logits, TopK, softmax over the kept logits
+ *     moe_permute     per-expert counts, exclusive scan, stable scatter/gather
+ *     moe_expert_ffn  grouped SwiGLU expert FFN over expert-contiguous rows
+ *     moe_combine     gate-weighted sum back in token order
+ *     moe_forward     all of the above in one call
+ *
+ * Conventions shared by every call
+ *  - Tensors are DEVICE pointers (hipMalloc'ed or torch CUDA/HIP tensors),
+ *    row-major and contiguous, each aligned to 16 bytes.
+ *  - Element type of x and of every weight: dims->dtype (MOE_F32 or MOE_BF16).
+ *    Accumulation is fp32 in every case.
+ *  - Ownership: the caller allocates and frees every buffer, the workspace
+ *    included. The library allocates nothing and keeps no pointer after a call
+ *    returns.
+ *  - Asynchrony: a call only enqueues kernels on `stream` (a hipStream_t passed
+ *    as void*, NULL = the default stream) and returns. Outputs are valid once
+ *    the stream reaches that point; inputs must stay alive until then. No call
+ *    synchronises or reads device memory on the host.
+ *  - Errors: arguments are validated before anything is launched. On a non-OK
+ *    status nothing has been enqueued and outputs are untouched (except
+ *    MOE_ERR_HIP, raised by a failed launch). moe_last_error() returns a
+ *    thread-local description of the last failure. T = 0 is valid: MOE_OK,
+ *    nothing is launched and no output is written. No C++ exception crosses this interface.
+ *  - Routing decisions are taken on fp32 logits; ties between equal logits go
+ *    to the lower expert index, and slot k = 0 holds the largest logit.
+ *  - Determinism: no call uses floating-point atomics; the same inputs give
+ *    bit-identical outputs on every run.
+ *  - Calls on different streams share no state and may run concurrently.
+ *
+ * Supported sizes: 1 <= E <= 64, 1 <= K <= min(E, 8), d and F multiples of 64,
+ * d <= 65536, T*K < 2^31. Other valid sizes return MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, negative or zero size, K > E, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* valid arguments outside the supported sizes listed above */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4          /* a HIP launch failed; see moe_last_error() */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem sizes. T tokens, model dim d, expert hidden dim F, E experts, K kept per token. */
+typedef struct {
+  int64_t T;
+  int32_t d, F, E, K;
+  int32_t dtype; /* moe_dtype of x and of all weights */
+} moe_dims;
+
+typedef struct {
+  const float* gate_bias; /* [E] fp32 added to the logits before TopK, or NULL (no bias) */
+  int32_t y_dtype;        /* moe_dtype of y; ignored when accumulate = 1 */
+  int32_t accumulate;     /* 0: y = result (rounded to y_dtype, nearest-even);
+                             1: y is fp32 and receives y += result (residual stream) */
+} moe_opts;
+
+/* Router (csdn explainer sections 2.1-2.3; xyznot.com "Método").
+ *   x        [T][d] dtype        token representations
+ *   w_gate   [d][E] dtype        router weight W_g (logits = x . W_g)
+ *   topk_idx [T][K] int32  out   kept experts, slot 0 = largest logit, ties -> lower index
+ *   topk_w   [T][K] fp32   out   softmax over the K kept logits (sums to 1 per token)
+ *   logits   [T][E] fp32   out   optional (NULL = not written): x . W_g + bias in fp32
+ * opts may be NULL (no bias). */
+moe_status moe_route(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate,
+                     int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+
+/* Token permutation into expert-contiguous order (variable tokens per expert:
+ * zh.newsflash.city article, mixture-of-experts layer section).
+ *   topk_idx  [T][K] int32 in    values in [0, E); the K experts of a token are distinct
+ *   x         [T][d] dtype in
+ *   counts    [E]    int32 out   tokens routed to each expert
+ *   offsets   [E+1]  int32 out   exclusive scan of counts; offsets[E] = T*K
+ *   row_token [T*K]  int32 out   token of each permuted row; rows of one expert follow
+ *                                ascending token index
+ *   token_row [T][K] int32 out   permuted row of (token, slot)
+ *   x_perm    [T*K][d] dtype out x_perm[r] = x[row_token[r]]; may be NULL (maps only)
+ * Out-of-range expert ids give undefined maps (not checked on the device). */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* row_token, int32_t* token_row, void* x_perm, void* stream);
+
+/* Grouped SwiGLU expert FFN (xyznot.com "Método" and "Términos clave").
+ * Rows [offsets[e], offsets[e+1]) of x_perm belong to expert e:
+ *   h_ws[r]   = silu(x_perm[r] . w1[e]^T) * (x_perm[r] . w3[e]^T)   (stored in dtype)
+ *   y_perm[r] = h_ws[r] . w2[e]^T                                    (fp32)
+ *   x_perm  [T*K][d] dtype     offsets [E+1] int32 (device)
+ *   w1, w3  [E][F][d] dtype    w2 [E][d][F] dtype
+ *   h_ws    [T*K][F] dtype     caller-provided scratch, overwritten
+ *   y_perm  [T*K][d] fp32 out
+ * Experts with no rows cost nothing. */
+moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w3, const void* w2, void* h_ws, float* y_perm, void* stream);
+
+/* Gate-weighted combine back to token order (csdn explainer section 1: y = sum_i G(x)_i E_i(x)).
+ *   y[t] = sum_{k=0..K-1} topk_w[t][k] * y_perm[token_row[t][k]], summed in fp32 in slot order
+ *   y_perm [T*K][d] fp32, token_row [T][K] int32, topk_w [T][K] fp32
+ *   y      [T][d]  opts->y_dtype, or fp32 with y += result when opts->accumulate = 1
+ * opts may be NULL (y_dtype = dims->dtype, no accumulation). */
+moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* y_perm, const int32_t* token_row,
+                       const float* topk_w, void* y, void* stream);
+
+/* Bytes of device workspace moe_forward needs for these sizes (0 for invalid dims). */
+size_t moe_workspace_bytes(const moe_dims* dims);
+
+/* The whole layer: route -> permute -> expert FFN -> combine, all on `stream`.
+ *   x [T][d] dtype, w_gate [d][E], w1/w3 [E][F][d], w2 [E][d][F] (dtype)
+ *   y [T][d] as in moe_combine (y may not alias x unless accumulate = 1 and y is a separate fp32 stream)
+ *   workspace: >= moe_workspace_bytes(dims) bytes of device memory, 256-byte aligned
+ * The token rows are gathered by the first expert matmul itself, so no x_perm copy is made. */
+moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
+                       const void* w3, const void* w2, void* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* RMSNorm of a residual stream for a stack of mixture-of-experts layers (the pages
+ * do not describe the norm; unit weight): x_bf16[t] = bf16(h[t] / sqrt(mean_j h[t][j]^2 + eps)),
+ * rounded to nearest even. h [T][d] fp32 in, x_bf16 [T][d] bf16 out. */
+moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream);
+
+/* Static name of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,253 @@
+// C ABI of the mixture-of-experts library (declarations and contracts in include/moe.h).
+// Validation runs before any launch; every call only enqueues kernels on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum : unsigned { USE_D = 1, USE_F = 2, USE_EK = 4, USE_DTYPE = 8 };
+
+moe_status check_dims(const moe_dims* dims, unsigned use) {
+  if (!dims) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+  const moe_dims& m = *dims;
+  if (m.T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld is negative", (long long)m.T);
+  if ((use & USE_D) && m.d <= 0) return fail(MOE_ERR_INVALID_ARG, "d = %d must be positive", m.d);
+  if ((use & USE_F) && m.F <= 0) return fail(MOE_ERR_INVALID_ARG, "F = %d must be positive", m.F);
+  if (use & USE_EK) {
+    if (m.E <= 0 || m.K <= 0) return fail(MOE_ERR_INVALID_ARG, "E = %d and K = %d must be positive", m.E, m.K);
+    if (m.K > m.E) return fail(MOE_ERR_INVALID_ARG, "K = %d exceeds E = %d", m.K, m.E);
+    if (m.E > moe::kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", m.E, moe::kMaxExperts);
+    if (m.K > moe::kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "K = %d > %d", m.K, moe::kMaxTopK);
+    if (m.T * (int64_t)m.K >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  }
+  if ((use & USE_DTYPE) && m.dtype != MOE_F32 && m.dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype = %d is not MOE_F32 or MOE_BF16", m.dtype);
+  if ((use & USE_D) && (m.d % 64 != 0 || m.d > 65536))
+    return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 64 and <= 65536", m.d);
+  if ((use & USE_F) && (m.F % 64 != 0 || m.F > (1 << 24)))
+    return fail(MOE_ERR_UNSUPPORTED, "F = %d must be a multiple of 64 and <= 2^24", m.F);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(MOE_ERR_INVALID_ARG, "%s is NULL", name) : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                \
+  do {                               \
+    moe_status s_ = (expr);          \
+    if (s_ != MOE_OK) return s_;     \
+  } while (0)
+
+moe_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Workspace {
+  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, h, y_perm, total;
+};
+
+Workspace layout(const moe_dims& m) {
+  const size_t S = (size_t)m.T * m.K;
+  Workspace w{};
+  size_t o = 0;
+  w.topk_idx = o;  o = align256(o + S * 4);
+  w.topk_w = o;    o = align256(o + S * 4);
+  w.counts = o;    o = align256(o + (size_t)m.E * 4);
+  w.offsets = o;   o = align256(o + (size_t)(m.E + 1) * 4);
+  w.row_token = o; o = align256(o + S * 4);
+  w.token_row = o; o = align256(o + S * 4);
+  w.h = o;         o = align256(o + S * (size_t)m.F * elem_bytes(m.dtype));
+  w.y_perm = o;    o = align256(o + S * (size_t)m.d * 4);
+  w.total = o;
+  return w;
+}
+
+const moe_opts kDefaultOpts = {nullptr, -1, 0};
+
+moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
+  const moe_opts& op = o ? *o : kDefaultOpts;
+  if (op.accumulate != 0 && op.accumulate != 1)
+    return fail(MOE_ERR_INVALID_ARG, "accumulate = %d must be 0 or 1", op.accumulate);
+  int yd = op.y_dtype;
+  if (!o) yd = m.dtype;
+  if (op.accumulate) yd = MOE_F32;
+  if (yd != MOE_F32 && yd != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "y_dtype = %d is not valid", yd);
+  *y_dtype = yd;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_STATUS_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_route(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate,
+                     int32_t* topk_idx, float* topk_w, float* logits, void* stream) {
+  MOE_TRY(check_dims(dims, USE_D | USE_EK | USE_DTYPE));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(logits, "logits", false));
+  const moe_dims& m = *dims;
+  if (m.T == 0) return MOE_OK;
+  moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
+                    logits, static_cast<hipStream_t>(stream));
+  return check_launch("moe_route");
+}
+
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* row_token, int32_t* token_row, void* x_perm, void* stream) {
+  MOE_TRY(check_dims(dims, USE_EK | (x_perm ? (USE_D | USE_DTYPE) : 0u)));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(counts, "counts"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(row_token, "row_token"));
+  MOE_TRY(check_ptr(token_row, "token_row"));
+  MOE_TRY(check_ptr(x_perm, "x_perm", false));
+  if (x_perm) MOE_TRY(check_ptr(x, "x"));
+  const moe_dims& m = *dims;
+  if (m.T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
+  MOE_TRY(check_launch("moe_permute (index)"));
+  if (x_perm) {
+    moe::launch_gather_rows(x, row_token, m.T * m.K, (int64_t)m.d * elem_bytes(m.dtype), x_perm, s);
+    MOE_TRY(check_launch("moe_permute (gather)"));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w3, const void* w2, void* h_ws, float* y_perm, void* stream) {
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE));
+  MOE_TRY(check_ptr(x_perm, "x_perm"));
+  MOE_TRY(check_ptr(offsets, "offsets"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(h_ws, "h_ws"));
+  MOE_TRY(check_ptr(y_perm, "y_perm"));
+  const moe_dims& m = *dims;
+  if (m.T == 0) return MOE_OK;
+  moe::launch_expert_ffn(m.dtype, x_perm, nullptr, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, w2, h_ws, y_perm,
+                         static_cast<hipStream_t>(stream));
+  return check_launch("moe_expert_ffn");
+}
+
+moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* y_perm, const int32_t* token_row,
+                       const float* topk_w, void* y, void* stream) {
+  MOE_TRY(check_dims(dims, USE_D | USE_EK | USE_DTYPE));
+  MOE_TRY(check_ptr(y_perm, "y_perm"));
+  MOE_TRY(check_ptr(token_row, "token_row"));
+  MOE_TRY(check_ptr(topk_w, "topk_w"));
+  MOE_TRY(check_ptr(y, "y"));
+  const moe_dims& m = *dims;
+  int yd = 0;
+  MOE_TRY(check_opts(m, opts, &yd));
+  if (m.T == 0) return MOE_OK;
+  moe::launch_combine(y_perm, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y,
+                      static_cast<hipStream_t>(stream));
+  return check_launch("moe_combine");
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims) {
+  if (check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE) != MOE_OK) return 0;
+  return layout(*dims).total;
+}
+
+moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
+                       const void* w3, const void* w2, void* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(y, "y"));
+  const moe_dims& m = *dims;
+  int yd = 0;
+  MOE_TRY(check_opts(m, opts, &yd));
+  if (m.T == 0) return MOE_OK;
+  const Workspace L = layout(m);
+  MOE_TRY(check_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + L.topk_idx);
+  float* topk_w = reinterpret_cast<float*>(ws + L.topk_w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  int32_t* token_row = reinterpret_cast<int32_t*>(ws + L.token_row);
+  void* h = ws + L.h;
+  float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
+                    nullptr, s);
+  MOE_TRY(check_launch("moe_forward (route)"));
+  moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
+  MOE_TRY(check_launch("moe_forward (permute)"));
+  moe::launch_expert_ffn(m.dtype, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, w2, h, y_perm, s);
+  MOE_TRY(check_launch("moe_forward (expert ffn)"));
+  moe::launch_combine(y_perm, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y, s);
+  return check_launch("moe_forward (combine)");
+}
+
+moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld is negative", (long long)T);
+  if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "d = %d must be positive", d);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+  if (d % 64 != 0 || d > 65536) return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 64", d);
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(x_bf16, "x_bf16"));
+  if (T == 0) return MOE_OK;
+  moe::launch_rmsnorm(h, T, d, eps, x_bf16, static_cast<hipStream_t>(stream));
+  return check_launch("moe_rmsnorm");
+}
+
+}  // extern "C"

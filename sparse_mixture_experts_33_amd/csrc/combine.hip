@@ -1,0 +1,95 @@
+// Gate-weighted combine back to token order, y = sum_i G(x)_i E_i(x) (blog.csdn.net explainer,
+// section 1; xyznot.com summary, "Método"): the expert outputs return to their original token
+// positions (zh.newsflash.city article, expert-parallel paragraph) and are added.
+//
+// One wavefront per token, 16-byte accesses along d. The K terms are added in fp32 in slot
+// order, s = w0*o0, then s = fma(w_k, o_k, s), so the result does not depend on scheduling.
+// HBM-bound: T*K*d*4 bytes read, T*d*|y| written (plus T*d*4 read when accumulating).
+//
+// Also the RMSNorm of a residual stream for stacks of such layers (the pages describe no norm;
+// unit weight): x = bf16(h / sqrt(mean(h^2) + eps)).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+template <int MODE>  // 0: y fp32, 1: y bf16, 2: y fp32 accumulate
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ token_row,
+                                                      const float* __restrict__ topk_w, int64_t T, int d, int K,
+                                                      void* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  int rows[kMaxTopK];
+  float g[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    rows[k] = (k < K) ? token_row[t * K + k] : 0;
+    g[k] = (k < K) ? topk_w[t * K + k] : 0.0f;
+  }
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    f32x4_t s = g[0] * *reinterpret_cast<const f32x4_t*>(y_perm + (int64_t)rows[0] * d + c);
+#pragma unroll
+    for (int k = 1; k < kMaxTopK; ++k) {
+      if (k < K) {
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(y_perm + (int64_t)rows[k] * d + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] = fmaf(g[k], o[q], s[q]);
+      }
+    }
+    if constexpr (MODE == 0) {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + t * d + c) = s;
+    } else if constexpr (MODE == 1) {
+      *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(y) + t * d + c) =
+          u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+    } else {
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + t * d + c);
+      *p = *p + s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int64_t T, int d, float eps,
+                                                      bf16_t* __restrict__ x) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = h + t * d;
+  float ss = 0.0f;
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+    ss = fmaf(v[0], v[0], ss);
+    ss = fmaf(v[1], v[1], ss);
+    ss = fmaf(v[2], v[2], ss);
+    ss = fmaf(v[3], v[3], ss);
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+    *reinterpret_cast<u32x2_t*>(x + t * d + c) = u32x2_t{pack_bf16x2(v[0] * inv, v[1] * inv),
+                                                         pack_bf16x2(v[2] * inv, v[3] * inv)};
+  }
+}
+
+}  // namespace
+
+void launch_combine(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K,
+                    int y_dtype, int accumulate, void* y, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (accumulate)
+    hipLaunchKernelGGL(combine_kernel<2>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+  else if (y_dtype == kBF16)
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+}
+
+void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(blocks), dim3(256), 0, stream, h, T, d, eps, static_cast<bf16_t*>(x_bf16));
+}
+
+}  // namespace moe

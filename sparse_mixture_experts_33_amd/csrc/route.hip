@@ -1,0 +1,190 @@
+// Router: logits = x . W_g (+ bias), TopK (the rest set to -inf), softmax over the kept logits.
+// Definitions: blog.csdn.net explainer of "Mixtral of Experts", sections 2.1-2.3; xyznot.com
+// summary, "Método" (n = 8, K = 2).
+//
+// Bandwidth kernel: it reads x once (T*d elements) and W_g (d*E elements, shared by every
+// token and served from L2). One wavefront owns TPW tokens; each lane covers 16-byte slices
+// of d and accumulates E partial sums per token in fp32. A butterfly over the 64 lanes gives
+// every lane the full logits; TopK is then repeated argmax over registers (ties -> lower
+// index) and the softmax uses only the K kept logits, so the other experts get exactly 0.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+template <typename T, int V>
+__device__ inline void unpack16(u32x4_t r, float (&v)[V]);
+
+template <>
+__device__ inline void unpack16<bf16_t, 8>(u32x4_t r, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(r[i]);
+    v[2 * i + 1] = bf16_hi(r[i]);
+  }
+}
+template <>
+__device__ inline void unpack16<float, 4>(u32x4_t r, float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+}
+
+// W_g row k (E contiguous values) as fp32. Vector path when E == 8.
+template <typename T, int EMAX>
+__device__ inline void load_gate_row(const T* row, int E, float (&w)[EMAX]) {
+  if constexpr (EMAX == 8) {
+    if (E == 8) {
+      if constexpr (sizeof(T) == 2) {
+        float t[8];
+        unpack16<bf16_t, 8>(load16(row), t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = t[e];
+      } else {
+        float t0[4], t1[4];
+        unpack16<float, 4>(load16(row), t0);
+        unpack16<float, 4>(load16(row + 4), t1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = t0[e];
+          w[e + 4] = t1[e];
+        }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) w[e] = (e < E) ? Elem<T>::to_f32(row[e]) : 0.0f;
+}
+
+template <int EMAX>
+__device__ inline void finalize_token(const float (&acc)[EMAX], int64_t t, int E, int K, const float* bias,
+                                      int32_t* topk_idx, float* topk_w, float* logits) {
+  float l[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) l[e] = (e < E) ? acc[e] + (bias ? bias[e] : 0.0f) : 0.0f;
+  if (logits) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) logits[t * E + e] = l[e];
+  }
+  uint64_t taken = 0;
+  int sel[kMaxTopK];
+  float sv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    sel[j] = 0;
+    sv[j] = 0.0f;
+    if (j < K) {
+      int best = -1;
+      float bv = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E && !((taken >> e) & 1ull) && (best < 0 || l[e] > bv)) {
+          best = e;
+          bv = l[e];
+        }
+      }
+      taken |= 1ull << best;
+      sel[j] = best;
+      sv[j] = bv;
+    }
+  }
+  // softmax over the kept logits, shifted by the largest (slot 0)
+  float ex[kMaxTopK];
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    ex[j] = (j < K) ? expf(sv[j] - sv[0]) : 0.0f;
+    s += ex[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < K) {
+      topk_idx[t * K + j] = sel[j];
+      topk_w[t * K + j] = ex[j] / s;
+    }
+  }
+}
+
+template <typename T, int EMAX, int TPW>
+__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, const T* __restrict__ wg,
+                                                    const float* __restrict__ bias, int64_t ntok, int d, int E,
+                                                    int K, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w, float* __restrict__ logits) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave)) * TPW;
+  if (t0 >= ntok) return;
+
+  float acc[TPW][EMAX];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[tt][e] = 0.0f;
+
+  for (int k0 = lane * V; k0 < d; k0 += kWave * V) {
+    float xv[TPW][V];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      if (t0 + tt < ntok) {
+        unpack16<T, V>(load16(x + (t0 + tt) * d + k0), xv[tt]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) xv[tt][j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float w[EMAX];
+      load_gate_row<T, EMAX>(wg + (int64_t)(k0 + j) * E, E, w);
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) acc[tt][e] = fmaf(xv[tt][j], w[e], acc[tt][e]);
+    }
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) acc[tt][e] = wave_sum(acc[tt][e]);
+
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+    if (lane == tt && t0 + tt < ntok) finalize_token<EMAX>(acc[tt], t0 + tt, E, K, bias, topk_idx, topk_w, logits);
+}
+
+template <typename T, int EMAX, int TPW>
+void launch(const void* x, const void* wg, const float* bias, int64_t T_, int d, int E, int K, int32_t* idx,
+            float* w, float* logits, hipStream_t s) {
+  const int64_t waves = (T_ + TPW - 1) / TPW;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
+  hipLaunchKernelGGL((route_kernel<T, EMAX, TPW>), dim3(blocks), dim3(256), 0, s, static_cast<const T*>(x),
+                     static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
+}
+
+template <typename T>
+void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int d, int E, int K, int32_t* idx,
+              float* w, float* logits, hipStream_t s) {
+  const bool many = T_ >= 4096;
+  if (E <= 8) {
+    if (many) launch<T, 8, 4>(x, wg, bias, T_, d, E, K, idx, w, logits, s);
+    else launch<T, 8, 1>(x, wg, bias, T_, d, E, K, idx, w, logits, s);
+  } else {
+    launch<T, 64, 1>(x, wg, bias, T_, d, E, K, idx, w, logits, s);
+  }
+}
+
+}  // namespace
+
+void launch_route(int dtype, const void* x, const void* w_gate, const float* bias, int64_t T, int d, int E, int K,
+                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream) {
+  if (dtype == kBF16)
+    launch_t<bf16_t>(x, w_gate, bias, T, d, E, K, topk_idx, topk_w, logits, stream);
+  else
+    launch_t<float>(x, w_gate, bias, T, d, E, K, topk_idx, topk_w, logits, stream);
+}
+
+}  // namespace moe

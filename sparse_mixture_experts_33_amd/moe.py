@@ -1,0 +1,157 @@
+"""Python binding of libmoe.so (C ABI in include/moe.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls and does nothing but turn
+torch tensors into device pointers, sizes into the ``moe_dims``/``moe_opts`` structs and
+the current torch stream into a ``hipStream_t``. All arithmetic runs in the library's HIP
+kernels; if the library is missing these functions raise instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+
+# every symbol include/moe.h declares
+SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_workspace_bytes", "moe_forward",
+           "moe_rmsnorm", "moe_status_string", "moe_last_error", "moe_abi_version")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("F", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class moe_opts(ctypes.Structure):
+    _fields_ = [("gate_bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    T: int
+    d: int
+    F: int
+    E: int
+    K: int
+    dtype: int  # MOE_F32 or MOE_BF16
+
+    def c(self) -> moe_dims:
+        return moe_dims(self.T, self.d, self.F, self.E, self.K, self.dtype)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built by sparse_mixture_experts_33_amd/build.py). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.moe_route.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp]
+        L.moe_permute.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_combine.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp]
+        L.moe_workspace_bytes.argtypes = [P(moe_dims)]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_forward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_rmsnorm.argtypes = [i64, i32, f32, vp, vp, vp]
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_abi_version.restype = i32
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_rmsnorm"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16):
+    return moe_opts(_ptr(gate_bias), dtype if y_dtype is None else y_dtype, 1 if accumulate else 0)
+
+
+def moe_route(dims: Dims, x, w_gate, topk_idx, topk_w, logits=None, gate_bias=None, stream=None):
+    o = _opts(gate_bias, dtype=dims.dtype)
+    _check(lib().moe_route(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(topk_idx),
+                           _ptr(topk_w), _ptr(logits), _stream(stream)))
+
+
+def moe_permute(dims: Dims, topk_idx, x, counts, offsets, row_token, token_row, x_perm=None, stream=None):
+    _check(lib().moe_permute(ctypes.byref(dims.c()), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+                             _ptr(row_token), _ptr(token_row), _ptr(x_perm), _stream(stream)))
+
+
+def moe_expert_ffn(dims: Dims, x_perm, offsets, w1, w3, w2, h_ws, y_perm, stream=None):
+    _check(lib().moe_expert_ffn(ctypes.byref(dims.c()), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2),
+                                _ptr(h_ws), _ptr(y_perm), _stream(stream)))
+
+
+def moe_combine(dims: Dims, y_perm, token_row, topk_w, y, y_dtype=None, accumulate=False, stream=None):
+    o = _opts(None, y_dtype, accumulate, dims.dtype)
+    _check(lib().moe_combine(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(y_perm), _ptr(token_row), _ptr(topk_w),
+                             _ptr(y), _stream(stream)))
+
+
+def moe_workspace_bytes(dims: Dims) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def moe_forward(dims: Dims, x, w_gate, w1, w3, w2, y, workspace, gate_bias=None, y_dtype=None, accumulate=False,
+                stream=None, workspace_bytes=None):
+    o = _opts(gate_bias, y_dtype, accumulate, dims.dtype)
+    nbytes = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
+    _check(lib().moe_forward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
+                             _ptr(w2), _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def moe_rmsnorm(T: int, d: int, eps: float, h, x_bf16, stream=None):
+    _check(lib().moe_rmsnorm(T, d, eps, _ptr(h), _ptr(x_bf16), _stream(stream)))
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())

@@ -1,0 +1,237 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: indices, counts, offsets and maps bit-exact (routing indices wherever the gap between
+the K-th and (K+1)-th logits exceeds 1e-4, slot order wherever the top-2 gap does; near-ties
+are reported and their selection checked for validity). Outputs: max|d|/max|y_ref| <= 2e-2
+for bf16 storage, <= 1e-5 for fp32. Gate weights and logits: absolute 1e-5 / 1e-4 (fp32 sums
+of d products of O(1/sqrt(d)) terms against double).
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from helpers import as_f64, dev, gaps, host, rel_err, say, selection_is_valid, tolerance
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TIE = 1e-4
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_mixture_experts_33_amd as moe
+    moe.lib()
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return moe
+
+
+def dims_of(M, w, T=None):
+    return M.Dims(w.T if T is None else T, w.d, w.F, w.E, w.K, M.MOE_BF16 if w.dtype == "bf16" else M.MOE_F32)
+
+
+SMALL = {
+    "tiny_f32": mi.WORKLOADS["tiny_f32"],
+    "ragged_bf16": mi.Workload("ragged_bf16", T=300, d=256, F=512, dtype="bf16", seed=611),
+    "ragged_f32": mi.Workload("ragged_f32", T=173, d=192, F=320, dtype="f32", seed=612),
+    "ragged_bf16_d192": mi.Workload("ragged_bf16_d192", T=97, d=192, F=448, dtype="bf16", seed=613),
+    "skew_small_bf16": mi.Workload("skew_small_bf16", T=515, d=128, F=256, dtype="bf16", skew_bias=True, seed=614),
+    "e16_k4_bf16": mi.Workload("e16_k4_bf16", T=130, d=128, F=192, E=16, K=4, dtype="bf16", seed=615),
+    "e1_k1_f32": mi.Workload("e1_k1_f32", T=70, d=128, F=128, E=1, K=1, dtype="f32", seed=616),
+    "e64_k8_f32": mi.Workload("e64_k8_f32", T=40, d=64, F=64, E=64, K=8, dtype="f32", seed=617),
+}
+
+
+class Layer:
+    """Inputs of one workload on host (numpy) and device (torch)."""
+
+    def __init__(self, w, x=None, W=None):
+        self.w = w
+        self.x = mi.tokens(w) if x is None else x
+        self.W = mi.layer_weights(w) if W is None else W
+        self.dx = dev(self.x)
+        self.dW = {k: dev(v) for k, v in self.W.items() if v is not None}
+        self.dbias = dev(self.W["bias"]) if self.W["bias"] is not None else None
+
+
+def gpu_route(M, L, T=None):
+    w = L.w
+    T = w.T if T is None else T
+    idx = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, w.E), dtype=torch.float32, device="cuda")
+    M.moe_route(dims_of(M, w, T), L.dx, L.dW["w_gate"], idx, wt, lg, gate_bias=L.dbias)
+    torch.cuda.synchronize()
+    return host(idx), host(wt), host(lg)
+
+
+def gpu_forward(M, L, accumulate=False, y0=None, y_dtype=None):
+    w = L.w
+    dm = dims_of(M, w)
+    ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    if accumulate:
+        y = dev(y0.astype(np.float32))
+    else:
+        y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device="cuda")
+    M.moe_forward(dm, L.dx, L.dW["w_gate"], L.dW["w1"], L.dW["w3"], L.dW["w2"], y, ws, gate_bias=L.dbias,
+                  accumulate=accumulate)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def check_routing(w, gi, gw, gl, ol, oi, ow):
+    """Returns the mask of tokens whose routing is decided (not a near-tie)."""
+    assert np.abs(gl.astype(np.float64) - ol).max() <= 1e-4
+    gapk, gap12 = gaps(ol, w.K)
+    decided = gapk > TIE
+    same_set = np.array([set(a) == set(b) for a, b in zip(gi.tolist(), oi.tolist())])
+    assert same_set[decided].all(), f"routing sets differ on {np.flatnonzero(decided & ~same_set)[:10]}"
+    ordered = decided & (gap12 > TIE)
+    # slot order is fixed (descending logit) wherever the logits are not near-tied
+    sorted_gap = np.diff(-np.sort(-ol, axis=1)[:, :w.K], axis=1)
+    order_ok = (np.abs(sorted_gap) > TIE).all(axis=1) if w.K > 1 else np.ones(w.T, bool)
+    strict = ordered & order_ok
+    assert np.array_equal(gi[strict], oi[strict])
+    assert np.abs(gw[strict] - ow[strict]).max(initial=0.0) <= 1e-5
+    assert np.allclose(gw.sum(1), 1.0, atol=1e-6)
+    for t in np.flatnonzero(~decided):
+        assert selection_is_valid(gi[t], ol[t], 2 * TIE), f"token {t}: invalid near-tie selection {gi[t]}"
+    n_ties = int((~decided).sum())
+    if n_ties:
+        say(f"  {w.name}: {n_ties} near-tie tokens (gap <= {TIE}); their selections are valid")
+    return decided
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route(M, name):
+    w = SMALL[name]
+    say(f"[route] {name} T={w.T} d={w.d} E={w.E} K={w.K} {w.dtype}")
+    L = Layer(w)
+    gi, gw, gl = gpu_route(M, L)
+    ol, oi, ow = oracle.route(L.x, L.W["w_gate"], w.K, bias=L.W["bias"])
+    check_routing(w, gi, gw, gl, ol, oi, ow)
+
+
+@pytest.mark.parametrize("T,E,K,skew", [(1, 8, 2, 0.0), (1000, 8, 2, 0.0), (1000, 8, 2, 3.0), (4097, 8, 2, 1.0),
+                                        (333, 16, 4, 2.0), (200, 64, 8, 0.0), (77, 1, 1, 0.0), (64, 8, 1, 5.0),
+                                        (16384, 8, 2, 2.0)])
+def test_permute(M, T, E, K, skew):
+    say(f"[permute] T={T} E={E} K={K} skew={skew}")
+    idx = mi.synthetic_routing(1000 + T + E, T, E, K, skew=skew)
+    d = 128
+    x = mi.normal(mi.key(77, 0, 0), (T, d), 1.0, "bf16")
+    dm = M.Dims(T, d, 64, E, K, M.MOE_BF16)
+    didx, dx = dev(idx), dev(x)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    row_token = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    token_row = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((T * K, d), dtype=torch.bfloat16, device="cuda")
+    M.moe_permute(dm, didx, dx, counts, offsets, row_token, token_row, x_perm)
+    torch.cuda.synchronize()
+    oc, oo, ort, otr = oracle.permute(idx, E)
+    assert np.array_equal(host(counts), oc)
+    assert np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(row_token), ort)
+    assert np.array_equal(host(token_row), otr)
+    assert np.array_equal(host(x_perm), oracle.gather(x, ort))
+
+
+def expert_ffn_case(M, w, skew, seed):
+    S = w.T * w.K
+    idx = mi.synthetic_routing(seed, w.T, w.E, w.K, skew=skew)
+    _, offsets, row_token, _ = oracle.permute(idx, w.E)
+    x = mi.tokens(w)
+    x_perm = oracle.gather(x, row_token)
+    W = mi.layer_weights(w)
+    dm = dims_of(M, w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    h = torch.empty((S, w.F), dtype=tdt, device="cuda")
+    y = torch.empty((S, w.d), dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(dm, dev(x_perm), dev(offsets), dev(W["w1"]), dev(W["w3"]), dev(W["w2"]), h, y)
+    torch.cuda.synchronize()
+    return host(y), x_perm, offsets, W
+
+
+@pytest.mark.parametrize("name,skew", [("tiny_f32", 0.0), ("ragged_bf16", 0.0), ("ragged_f32", 4.0),
+                                       ("ragged_bf16_d192", 2.0), ("e16_k4_bf16", 1.0), ("e1_k1_f32", 0.0),
+                                       ("e64_k8_f32", 0.0)])
+def test_expert_ffn(M, name, skew):
+    w = SMALL[name]
+    say(f"[expert_ffn] {name} skew={skew}")
+    y, x_perm, offsets, W = expert_ffn_case(M, w, skew, 2000 + w.T)
+    ref = oracle.expert_ffn(x_perm, offsets, W["w1"], W["w3"], W["w2"])
+    err = rel_err(y, ref)
+    say(f"  max|d|/max|ref| = {err:.3e}")
+    assert err <= tolerance(w.dtype)
+
+
+@pytest.mark.parametrize("K,y_dtype,acc", [(2, "bf16", False), (2, "f32", False), (2, "f32", True), (1, "bf16", False),
+                                           (8, "f32", False)])
+def test_combine(M, K, y_dtype, acc):
+    T, d, E = 513, 256, 8 if K <= 8 else K
+    say(f"[combine] T={T} K={K} y={y_dtype} acc={acc}")
+    idx = mi.synthetic_routing(3000 + K, T, E, K)
+    _, _, _, token_row = oracle.permute(idx, E)
+    y_perm = mi.normal(mi.key(31, 0, 1), (T * K, d), 1.0, "f32")
+    g = np.abs(mi.normal(mi.key(31, 0, 2), (T, K), 1.0, "f32")) + 0.1
+    g = (g / g.sum(1, keepdims=True)).astype(np.float32)
+    y0 = mi.normal(mi.key(31, 0, 3), (T, d), 1.0, "f32")
+    dm = M.Dims(T, d, 64, E, K, M.MOE_BF16 if y_dtype == "bf16" else M.MOE_F32)
+    if acc:
+        y = dev(y0)
+    else:
+        y = torch.empty((T, d), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32, device="cuda")
+    M.moe_combine(dm, dev(y_perm), dev(token_row), dev(g), y, y_dtype=M.MOE_BF16 if y_dtype == "bf16" else M.MOE_F32,
+                  accumulate=acc)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y_perm, token_row, g) + (y0.astype(np.float64) if acc else 0.0)
+    got = as_f64(host(y))
+    if y_dtype == "bf16":
+        # fp32 sum then one round to nearest bf16: within one bf16 ulp of the exact value
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    else:
+        assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def check_forward(M, L, tokens=None, accumulate=False):
+    w = L.w
+    y0 = mi.normal(mi.key(41, 0, 0), (w.T, w.d), 1.0, "f32") if accumulate else None
+    y = gpu_forward(M, L, accumulate=accumulate, y0=y0)
+    r = oracle.forward(L.x, L.W["w_gate"], L.W["w1"], L.W["w3"], L.W["w2"], w.K, bias=L.W["bias"], tokens=tokens)
+    sel = np.arange(w.T) if tokens is None else tokens
+    ref = r["y"] + (y0[sel].astype(np.float64) if accumulate else 0.0)
+    gapk, _ = gaps(r["logits"], w.K)
+    keep = gapk > TIE
+    if (~keep).any():
+        say(f"  {(~keep).sum()} near-tie tokens excluded from the output comparison")
+    err = rel_err(y[sel][keep], ref[keep])
+    say(f"  {w.name}: forward max|d|/max|ref| = {err:.3e} over {keep.sum()} tokens")
+    tol = tolerance(w.dtype) if not accumulate else 1e-5 if w.dtype == "f32" else tolerance(w.dtype)
+    assert err <= tol
+    return y
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(M, name):
+    w = SMALL[name]
+    say(f"[forward] {name}")
+    check_forward(M, Layer(w))
+
+
+def test_forward_accumulate_bf16(M):
+    w = SMALL["ragged_bf16"]
+    say("[forward] accumulate into an fp32 stream")
+    check_forward(M, Layer(w), accumulate=True)
+
+
+def test_forward_decode_full(M):
+    """Mixtral-shaped decode step (T=32, d=4096, F=14336, bf16): every token against the oracle."""
+    w = mi.WORKLOADS["decode_T32"]
+    say(f"[forward] {w.name} (full size, all tokens)")
+    L = Layer(w)
+    gi, gw, gl = gpu_route(M, L)
+    ol, oi, ow = oracle.route(L.x, L.W["w_gate"], w.K)
+    check_routing(w, gi, gw, gl, ol, oi, ow)
+    check_forward(M, L)
