@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the Mixtral-shaped sparse mixture-of-experts layer on one MI355X.
+
+One step = one moe_forward call (route -> permute -> grouped expert GEMMs -> combine) over one
+batch of seeded synthetic tokens that are already resident in HBM. The default workload is the
+decode step (T=32 tokens, d=4096, F=14336, E=8, K=2, bf16): HBM-bound, every expert's weights
+stream once. Other workloads (--workload) are reported the same way.
+
+Prints ONE JSON line: tokens/s for the whole step, the roofline of the dominant kernel (timed
+live with HIP events recorded by the library around that kernel inside the timed region) and
+the CPU oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + TFLOP/s or HBM GB/s vs peak (E=8,K=2,d=4096,F=14336)"
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3         # fp32 MFMA/vector
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode_T32")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU-oracle sample time")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--probe", choices=["copy"], help="plain copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_per_copy": n, "copies": 3}), flush=True)
+
+
+def source_digest() -> str:
+    """sha256 of the kernel sources (a counter summary is only valid for the source it was taken on)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_33_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_digest:\s*(\w+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != source_digest():
+        return None
+    return float(b.group(1))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the data-parallel layer needs no exchange between GPUs, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_33_amd as moe
+    from sparse_mixture_experts_33_amd.moe import MOE_STAGE_EXPERT_UP, stage_event_array
+
+    torch.cuda.set_device(0)
+    if args.probe == "copy":
+        copy_probe()
+        return
+
+    w = mi.WORKLOADS[args.workload]
+    dt = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    s_x = 2 if w.dtype == "bf16" else 4
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    dims = moe.Dims(w.T, w.d, w.F, w.E, w.K, dt, moe.MOE_LAYOUT_PACKED)
+
+    def packed(a, which):
+        # one-time weight rearrangement at load time (like converting a checkpoint), not timed
+        out = torch.empty_like(a)
+        moe.moe_pack_weights(dims, which, a, out)
+        torch.cuda.synchronize()
+        return out
+
+    t_gen = time.time()
+    layers = []
+    host_layer0 = None
+    for layer in range(w.layers):
+        W = mi.layer_weights(w, layer)
+        L = {k: (dev(v) if v is not None else None) for k, v in W.items()}
+        L["w1"] = packed(L["w1"], moe.MOE_W_UP)
+        L["w3"] = packed(L["w3"], moe.MOE_W_UP)
+        L["w2"] = packed(L["w2"], moe.MOE_W_DOWN)
+        layers.append(L)
+        if layer == 0:
+            host_layer0 = W
+        else:
+            del W
+    x_host = mi.tokens(w)
+    x = dev(x_host)
+    h0 = dev(mi.residual0(w)) if w.layers > 1 else None
+    log(f"[bench] {w.name}: inputs generated and resident in HBM in {time.time() - t_gen:.1f}s")
+
+    ws = torch.empty(moe.moe_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # routing of layer 0 (untimed) to count the experts that receive tokens
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    L0 = layers[0]
+    moe.moe_route(dims, x, L0["w_gate"], idx, wt, gate_bias=L0["bias"])
+    counts = torch.bincount(idx.flatten().long(), minlength=w.E).cpu().numpy()
+    active = int((counts > 0).sum())
+
+    if w.layers == 1:
+        y = torch.empty((w.T, w.d), dtype=tdt, device="cuda")
+    else:
+        h = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda")
+        xn = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+
+    def step(events=None):
+        if w.layers == 1:
+            moe.moe_forward(dims, x, L0["w_gate"], L0["w1"], L0["w3"], L0["w2"], y, ws, gate_bias=L0["bias"],
+                            stage_events=events)
+        else:
+            h.copy_(h0)
+            for li, L in enumerate(layers):
+                moe.moe_rmsnorm(w.T, w.d, w.eps, h, xn)
+                moe.moe_forward(dims, xn, L["w_gate"], L["w1"], L["w3"], L["w2"], h, ws, gate_bias=L["bias"],
+                                accumulate=True, stage_events=events if li == 0 else None)
+
+    # one pair of events per timed step around the dominant kernel (grouped GEMM 1 + SwiGLU)
+    ev = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ev_arrays = [stage_event_array({2 * MOE_STAGE_EXPERT_UP: a.cuda_event, 2 * MOE_STAGE_EXPERT_UP + 1: b.cuda_event})
+                 for a, b in ev]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_step = elapsed * 1e3 / args.steps
+    tokens_s = w.T * args.steps / elapsed
+    up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # algorithmic work per step (only routed experts count)
+    S = w.T * w.K
+    flops_layer = 2 * w.T * w.d * w.E + 6 * S * w.d * w.F
+    bytes_layer = active * 3 * w.d * w.F * s_x + w.d * w.E * s_x + w.T * w.d * s_x + w.T * w.d * (4 if w.layers > 1 else s_x)
+    step_flops = flops_layer * w.layers
+    step_bytes = bytes_layer * w.layers
+    # dominant kernel: grouped GEMM 1 (w1 and w3 of each routed expert, fused SwiGLU)
+    up_flops = 4 * S * w.d * w.F
+    up_bytes = active * 2 * w.F * w.d * s_x + S * w.d * s_x + S * w.F * s_x
+    intensity = up_flops / up_bytes
+    peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    hbm_bound = intensity < peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved = up_bytes / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = up_flops / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4)}
+    tr = stored_traffic("expert_up", w.name)
+    roof["traffic"] = tr
+    roof["kernel"] = "expert_up (grouped GEMM w1,w3 + SwiGLU)"
+    roof["kernel_ms"] = round(up_ms, 4)
+    roof["algorithmic"] = {"bytes": up_bytes, "flops": up_flops}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "F": w.F, "E": w.E, "K": w.K, "layers": w.layers,
+                   "router_bias": "1.5*ln(1/(e+1))" if w.skew_bias else None, "active_experts": active,
+                   "weight_layout": "fragment-packed (moe_pack_weights, at load time)",
+                   "parallelism": "single GPU"},
+        "step_tflops": round(step_flops / (ms_step * 1e-3) / 1e12, 2),
+        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_mfma": round(step_flops / (ms_step * 1e-3) / 1e12 / peak_tf, 4),
+        "step_frac_hbm": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x_host, host_layer0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, x_host, W, seconds):
+    """The CPU oracle (fp64, plain loops, host threads) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    sample = np.arange(min(w.T, 32), dtype=np.int64) if w.T <= 32 else np.linspace(0, w.T - 1, 16).astype(np.int64)
+    done, t0 = 0, time.perf_counter()
+    reps = 0
+    while True:
+        oracle.forward(x_host, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, bias=W["bias"], tokens=sample,
+                       threads=threads)
+        done += len(sample)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    note = f"{len(sample)} tokens of layer 0 x {reps} repetitions ({el:.1f}s)"
+    if w.layers > 1:
+        note += "; one layer of the stack, so tokens/s is per layer"
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": note}
+
+
+if __name__ == "__main__":
+    main()

@@ -68,11 +68,17 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+typedef enum {
+  MOE_LAYOUT_ROWMAJOR = 0, /* w1, w3 [E][F][d] and w2 [E][d][F], row-major */
+  MOE_LAYOUT_PACKED = 1    /* the fragment-packed layout written by moe_pack_weights (below) */
+} moe_layout;
+
 /* Problem sizes. T tokens, model dim d, expert hidden dim F, E experts, K kept per token. */
 typedef struct {
   int64_t T;
   int32_t d, F, E, K;
-  int32_t dtype; /* moe_dtype of x and of all weights */
+  int32_t dtype;         /* moe_dtype of x and of all weights */
+  int32_t weight_layout; /* moe_layout of w1, w3, w2 (w_gate is always [d][E] row-major) */
 } moe_dims;
 
 typedef struct {
@@ -80,7 +86,21 @@ typedef struct {
   int32_t y_dtype;        /* moe_dtype of y; ignored when accumulate = 1 */
   int32_t accumulate;     /* 0: y = result (rounded to y_dtype, nearest-even);
                              1: y is fp32 and receives y += result (residual stream) */
+  void* const* stage_events; /* optional instrumentation for moe_forward, or NULL: an array of
+                                2 * MOE_NUM_STAGES hipEvent_t (passed as void*, created by the
+                                caller); entry 2s is recorded on the stream just before stage s
+                                is launched and entry 2s+1 just after it. NULL entries are skipped. */
 } moe_opts;
+
+/* Stages of moe_forward, in launch order (one kernel each). */
+enum {
+  MOE_STAGE_ROUTE = 0,       /* logits, TopK, softmax */
+  MOE_STAGE_PERMUTE = 1,     /* counts, offsets, stable row maps */
+  MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1) */
+  MOE_STAGE_EXPERT_DOWN = 3, /* hidden x w2 (grouped GEMM 2) */
+  MOE_STAGE_COMBINE = 4,     /* gate-weighted sum back to token order */
+  MOE_NUM_STAGES = 5
+};
 
 /* Router (csdn explainer sections 2.1-2.3; xyznot.com "Método").
  *   x        [T][d] dtype        token representations
@@ -111,7 +131,7 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void
  *   h_ws[r]   = silu(x_perm[r] . w1[e]^T) * (x_perm[r] . w3[e]^T)   (stored in dtype)
  *   y_perm[r] = h_ws[r] . w2[e]^T                                    (fp32)
  *   x_perm  [T*K][d] dtype     offsets [E+1] int32 (device)
- *   w1, w3  [E][F][d] dtype    w2 [E][d][F] dtype
+ *   w1, w3  [E][F][d] dtype    w2 [E][d][F] dtype   (or packed: dims->weight_layout)
  *   h_ws    [T*K][F] dtype     caller-provided scratch, overwritten
  *   y_perm  [T*K][d] fp32 out
  * Experts with no rows cost nothing. */
@@ -126,11 +146,30 @@ moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_
 moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* y_perm, const int32_t* token_row,
                        const float* topk_w, void* y, void* stream);
 
+/* Expert weights in the fragment-packed layout (MOE_LAYOUT_PACKED).
+ *
+ * A matrix W[E][N][K] (row-major; N, K multiples of 16 and 4V) is stored as 1 KB fragments of
+ * 16 rows x 4V columns, V = 16 / element size (8 for bf16, 4 for fp32). Element W[e][n][k] goes to
+ *     ((e*(N/16) + n/16) * (K/(4V)) + k/(4V)) * 64V  +  lane*V  +  k%V,
+ *     lane = n%16 + 16 * ((k/V) % 4).
+ * Each fragment is one wavefront's matrix-core operand in lane order, and the fragments of one
+ * 16-row block follow each other along k, so a wavefront streaming that block reads one
+ * contiguous region with 1 KB per load instruction (the row-major rows of a block are K*elem
+ * bytes apart, which keeps many more DRAM pages open at once). Packing is a one-time
+ * rearrangement of the weights (same size); the packed and row-major paths give bit-identical
+ * results.
+ *   which = MOE_W_UP:   w (w1 or w3) [E][F][d]  (N = F, K = d)
+ *   which = MOE_W_DOWN: w (w2)       [E][d][F]  (N = d, K = F)
+ * w and w_packed are device buffers of E*F*d elements of dims->dtype and must not overlap. */
+enum { MOE_W_UP = 0, MOE_W_DOWN = 1 };
+moe_status moe_pack_weights(const moe_dims* dims, int32_t which, const void* w, void* w_packed, void* stream);
+
 /* Bytes of device workspace moe_forward needs for these sizes (0 for invalid dims). */
 size_t moe_workspace_bytes(const moe_dims* dims);
 
 /* The whole layer: route -> permute -> expert FFN -> combine, all on `stream`.
- *   x [T][d] dtype, w_gate [d][E], w1/w3 [E][F][d], w2 [E][d][F] (dtype)
+ *   x [T][d] dtype, w_gate [d][E], w1/w3 [E][F][d], w2 [E][d][F] (dtype; w1/w3/w2 packed when
+ *   dims->weight_layout = MOE_LAYOUT_PACKED)
  *   y [T][d] as in moe_combine (y may not alias x unless accumulate = 1 and y is a separate fp32 stream)
  *   workspace: >= moe_workspace_bytes(dims) bytes of device memory, 256-byte aligned
  * The token rows are gathered by the first expert matmul itself, so no x_perm copy is made. */

@@ -21,7 +21,7 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum : unsigned { USE_D = 1, USE_F = 2, USE_EK = 4, USE_DTYPE = 8 };
+enum : unsigned { USE_D = 1, USE_F = 2, USE_EK = 4, USE_DTYPE = 8, USE_LAYOUT = 16 };
 
 moe_status check_dims(const moe_dims* dims, unsigned use) {
   if (!dims) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
@@ -42,6 +42,8 @@ moe_status check_dims(const moe_dims* dims, unsigned use) {
     return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 64 and <= 65536", m.d);
   if ((use & USE_F) && (m.F % 64 != 0 || m.F > (1 << 24)))
     return fail(MOE_ERR_UNSUPPORTED, "F = %d must be a multiple of 64 and <= 2^24", m.F);
+  if ((use & USE_LAYOUT) && m.weight_layout != MOE_LAYOUT_ROWMAJOR && m.weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "weight_layout = %d is not a moe_layout", m.weight_layout);
   return MOE_OK;
 }
 
@@ -87,7 +89,7 @@ Workspace layout(const moe_dims& m) {
   return w;
 }
 
-const moe_opts kDefaultOpts = {nullptr, -1, 0};
+const moe_opts kDefaultOpts = {nullptr, -1, 0, nullptr};
 
 moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
   const moe_opts& op = o ? *o : kDefaultOpts;
@@ -159,7 +161,7 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void
 
 moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_t* offsets, const void* w1,
                           const void* w3, const void* w2, void* h_ws, float* y_perm, void* stream) {
-  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE));
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT));
   MOE_TRY(check_ptr(x_perm, "x_perm"));
   MOE_TRY(check_ptr(offsets, "offsets"));
   MOE_TRY(check_ptr(w1, "w1"));
@@ -169,9 +171,12 @@ moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_
   MOE_TRY(check_ptr(y_perm, "y_perm"));
   const moe_dims& m = *dims;
   if (m.T == 0) return MOE_OK;
-  moe::launch_expert_ffn(m.dtype, x_perm, nullptr, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, w2, h_ws, y_perm,
-                         static_cast<hipStream_t>(stream));
-  return check_launch("moe_expert_ffn");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::launch_expert_up(m.dtype, m.weight_layout, x_perm, nullptr, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h_ws,
+                        s);
+  MOE_TRY(check_launch("moe_expert_ffn (up)"));
+  moe::launch_expert_down(m.dtype, m.weight_layout, h_ws, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, s);
+  return check_launch("moe_expert_ffn (down)");
 }
 
 moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* y_perm, const int32_t* token_row,
@@ -190,6 +195,25 @@ moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* 
   return check_launch("moe_combine");
 }
 
+moe_status moe_pack_weights(const moe_dims* dims, int32_t which, const void* w, void* w_packed, void* stream) {
+  if (!dims) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+  const moe_dims& m = *dims;
+  if (m.E <= 0) return fail(MOE_ERR_INVALID_ARG, "E = %d must be positive", m.E);
+  if (m.E > moe::kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", m.E, moe::kMaxExperts);
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_DTYPE));
+  if (which != MOE_W_UP && which != MOE_W_DOWN) return fail(MOE_ERR_INVALID_ARG, "which = %d is not valid", which);
+  MOE_TRY(check_ptr(w, "w"));
+  MOE_TRY(check_ptr(w_packed, "w_packed"));
+  const size_t bytes = (size_t)m.E * m.F * m.d * elem_bytes(m.dtype);
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(w_packed);
+  if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+  const int N = which == MOE_W_UP ? m.F : m.d;
+  const int K = which == MOE_W_UP ? m.d : m.F;
+  moe::launch_pack_weights(m.dtype, w, m.E, N, K, w_packed, static_cast<hipStream_t>(stream));
+  return check_launch("moe_pack_weights");
+}
+
 size_t moe_workspace_bytes(const moe_dims* dims) {
   if (check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE) != MOE_OK) return 0;
   return layout(*dims).total;
@@ -198,7 +222,7 @@ size_t moe_workspace_bytes(const moe_dims* dims) {
 moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
                        const void* w3, const void* w2, void* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE));
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT));
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(w_gate, "w_gate"));
   MOE_TRY(check_ptr(w1, "w1"));
@@ -227,15 +251,34 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  void* const* ev = opts ? opts->stage_events : nullptr;
+  auto mark = [&](int i) -> moe_status {
+    if (!ev || !ev[i]) return MOE_OK;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+    return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  };
+
+  MOE_TRY(mark(2 * MOE_STAGE_ROUTE));
   moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
                     nullptr, s);
   MOE_TRY(check_launch("moe_forward (route)"));
+  MOE_TRY(mark(2 * MOE_STAGE_ROUTE + 1));
+  MOE_TRY(mark(2 * MOE_STAGE_PERMUTE));
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   MOE_TRY(check_launch("moe_forward (permute)"));
-  moe::launch_expert_ffn(m.dtype, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, w2, h, y_perm, s);
-  MOE_TRY(check_launch("moe_forward (expert ffn)"));
+  MOE_TRY(mark(2 * MOE_STAGE_PERMUTE + 1));
+  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_UP));
+  moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);
+  MOE_TRY(check_launch("moe_forward (expert up)"));
+  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_UP + 1));
+  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN));
+  moe::launch_expert_down(m.dtype, m.weight_layout, h, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, s);
+  MOE_TRY(check_launch("moe_forward (expert down)"));
+  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN + 1));
+  MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
   moe::launch_combine(y_perm, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y, s);
-  return check_launch("moe_forward (combine)");
+  MOE_TRY(check_launch("moe_forward (combine)"));
+  return mark(2 * MOE_STAGE_COMBINE + 1);
 }
 
 moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream) {

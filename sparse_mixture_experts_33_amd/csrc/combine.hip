@@ -2,7 +2,7 @@
 // section 1; xyznot.com summary, "Método"): the expert outputs return to their original token
 // positions (zh.newsflash.city article, expert-parallel paragraph) and are added.
 //
-// One wavefront per token, 16-byte accesses along d. The K terms are added in fp32 in slot
+// One wavefront (or, for few tokens, one workgroup) per token, 16-byte accesses along d. The K terms are added in fp32 in slot
 // order, s = w0*o0, then s = fma(w_k, o_k, s), so the result does not depend on scheduling.
 // HBM-bound: T*K*d*4 bytes read, T*d*|y| written (plus T*d*4 read when accumulating).
 //
@@ -14,13 +14,17 @@
 namespace moe {
 namespace {
 
-template <int MODE>  // 0: y fp32, 1: y bf16, 2: y fp32 accumulate
+// MODE 0: y fp32, 1: y bf16, 2: y fp32 accumulate. TPB tokens per 256-thread block: 4 (one
+// wavefront per token) for many tokens, 1 (the whole block on one token, all loads in flight at
+// once) for few tokens.
+template <int MODE, int TPB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ token_row,
                                                       const float* __restrict__ topk_w, int64_t T, int d, int K,
                                                       void* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  constexpr int NT = 256 / TPB;  // threads per token
+  const int lt = threadIdx.x % NT;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / NT;
   if (t >= T) return;
   int rows[kMaxTopK];
   float g[kMaxTopK];
@@ -29,7 +33,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     rows[k] = (k < K) ? token_row[t * K + k] : 0;
     g[k] = (k < K) ? topk_w[t * K + k] : 0.0f;
   }
-  for (int c = lane * 4; c < d; c += kWave * 4) {
+  for (int c = lt * 4; c < d; c += NT * 4) {
     f32x4_t s = g[0] * *reinterpret_cast<const f32x4_t*>(y_perm + (int64_t)rows[0] * d + c);
 #pragma unroll
     for (int k = 1; k < kMaxTopK; ++k) {
@@ -48,6 +52,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + t * d + c);
       *p = *p + s;
     }
+  }
+}
+
+template <int MODE>
+void launch_mode(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K, void* y,
+                 hipStream_t stream) {
+  if (T <= 1024) {
+    hipLaunchKernelGGL((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, token_row, topk_w,
+                       T, d, K, y);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<MODE, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, y_perm,
+                       token_row, topk_w, T, d, K, y);
   }
 }
 
@@ -78,13 +94,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 void launch_combine(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K,
                     int y_dtype, int accumulate, void* y, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((T + 3) / 4);
   if (accumulate)
-    hipLaunchKernelGGL(combine_kernel<2>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+    launch_mode<2>(y_perm, token_row, topk_w, T, d, K, y, stream);
   else if (y_dtype == kBF16)
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+    launch_mode<1>(y_perm, token_row, topk_w, T, d, K, y, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3(blocks), dim3(256), 0, stream, y_perm, token_row, topk_w, T, d, K, y);
+    launch_mode<0>(y_perm, token_row, topk_w, T, d, K, y, stream);
 }
 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream) {

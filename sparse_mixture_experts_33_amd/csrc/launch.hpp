@@ -8,6 +8,8 @@ namespace moe {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
+constexpr int kRowMajor = 0;
+constexpr int kPacked = 1;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 64;
 
@@ -20,12 +22,19 @@ void launch_permute_index(const int32_t* topk_idx, int64_t T, int E, int K, int3
 void launch_gather_rows(const void* x, const int32_t* row_token, int64_t rows, int64_t row_bytes, void* x_perm,
                         hipStream_t stream);
 
-// Expert FFN over expert-contiguous rows. row_src == nullptr: activation row r is act[r];
-// otherwise act[row_src[r]] (the gather of the permutation fused into the first matmul).
-// expected_rows_per_expert (T*K/E) picks the tile shape; any routing is handled correctly.
-void launch_expert_ffn(int dtype, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
-                       int d, int F, int E, const void* w1, const void* w3, const void* w2, void* h, float* y_perm,
-                       hipStream_t stream);
+// Expert FFN over expert-contiguous rows, as two grouped GEMMs.
+// up:   h[r] = silu(act[src(r)] . w1[e]^T) * (act[src(r)] . w3[e]^T), src(r) = row_src ? row_src[r] : r
+//       (row_src carries the permutation's gather into the first matmul)
+// down: y_perm[r] = h[r] . w2[e]^T
+// rows = T*K; the tile shape is chosen from rows/E, and any routing is handled correctly.
+// layout: kRowMajor or kPacked (fragment-packed weights, see moe_pack_weights in moe.h).
+void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row_src, const int32_t* offsets,
+                      int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
+                        int E, const void* w2, float* y_perm, hipStream_t stream);
+
+// Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
+void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_packed, hipStream_t stream);
 
 void launch_combine(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K,
                     int y_dtype, int accumulate, void* y, hipStream_t stream);

@@ -156,6 +156,47 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
     if (lane == tt && t0 + tt < ntok) finalize_token<EMAX>(acc[tt], t0 + tt, E, K, bias, topk_idx, topk_w, logits);
 }
 
+// Few tokens (decode): one workgroup per token, so all loads of a token are in flight at once.
+// Each of the 256 threads covers 16-byte slices of d; partial sums are reduced across each wave
+// (butterfly) and then across the 4 waves in LDS, in a fixed order.
+template <typename T, int EMAX>
+__global__ __launch_bounds__(256) void route_token_kernel(const T* __restrict__ x, const T* __restrict__ wg,
+                                                          const float* __restrict__ bias, int64_t ntok, int d,
+                                                          int E, int K, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w, float* __restrict__ logits) {
+  constexpr int V = 16 / sizeof(T);
+  __shared__ float part[4][EMAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x / kWave;
+  const int64_t t = blockIdx.x;
+  float acc[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
+  for (int k0 = threadIdx.x * V; k0 < d; k0 += 256 * V) {
+    float xv[V];
+    unpack16<T, V>(load16(x + t * d + k0), xv);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float w[EMAX];
+      load_gate_row<T, EMAX>(wg + (int64_t)(k0 + j) * E, E, w);
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) acc[e] = fmaf(xv[j], w[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e)
+    if (e < E) acc[e] = wave_sum(acc[e]);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+    finalize_token<EMAX>(acc, t, E, K, bias, topk_idx, topk_w, logits);
+  }
+}
+
 template <typename T, int EMAX, int TPW>
 void launch(const void* x, const void* wg, const float* bias, int64_t T_, int d, int E, int K, int32_t* idx,
             float* w, float* logits, hipStream_t s) {
@@ -169,6 +210,11 @@ template <typename T>
 void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int d, int E, int K, int32_t* idx,
               float* w, float* logits, hipStream_t s) {
   const bool many = T_ >= 4096;
+  if (T_ <= 512 && E <= 8) {
+    hipLaunchKernelGGL((route_token_kernel<T, 8>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
+                       static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
+    return;
+  }
   if (E <= 8) {
     if (many) launch<T, 8, 4>(x, wg, bias, T_, d, E, K, idx, w, logits, s);
     else launch<T, 8, 1>(x, wg, bias, T_, d, E, K, idx, w, logits, s);

@@ -15,11 +15,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
+MOE_W_UP, MOE_W_DOWN = 0, 1
+MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_COMBINE = range(5)
+MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 
 # every symbol include/moe.h declares
-SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_workspace_bytes", "moe_forward",
-           "moe_rmsnorm", "moe_status_string", "moe_last_error", "moe_abi_version")
+SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_workspace_bytes",
+           "moe_forward", "moe_rmsnorm", "moe_status_string", "moe_last_error", "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -30,11 +34,12 @@ class MoeError(RuntimeError):
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("F", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class moe_opts(ctypes.Structure):
-    _fields_ = [("gate_bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+    _fields_ = [("gate_bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
+                ("stage_events", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -45,9 +50,10 @@ class Dims:
     E: int
     K: int
     dtype: int  # MOE_F32 or MOE_BF16
+    layout: int = MOE_LAYOUT_ROWMAJOR  # of w1, w3, w2
 
     def c(self) -> moe_dims:
-        return moe_dims(self.T, self.d, self.F, self.E, self.K, self.dtype)
+        return moe_dims(self.T, self.d, self.F, self.E, self.K, self.dtype, self.layout)
 
 
 _lib = None
@@ -66,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.moe_permute.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp]
+        L.moe_pack_weights.argtypes = [P(moe_dims), i32, vp, vp, vp]
         L.moe_workspace_bytes.argtypes = [P(moe_dims)]
         L.moe_workspace_bytes.restype = sz
         L.moe_forward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -74,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
-        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_rmsnorm"):
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_forward",
+                     "moe_rmsnorm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -102,8 +110,20 @@ def _check(status: int):
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16):
-    return moe_opts(_ptr(gate_bias), dtype if y_dtype is None else y_dtype, 1 if accumulate else 0)
+def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16, stage_events=None):
+    return moe_opts(_ptr(gate_bias), dtype if y_dtype is None else y_dtype, 1 if accumulate else 0,
+                    stage_events)
+
+
+def stage_event_array(events: dict):
+    """ctypes array of 2*MOE_NUM_STAGES hipEvent_t handles for moe_opts.stage_events.
+
+    events maps an array position (2*stage for "before", 2*stage+1 for "after") to a raw
+    hipEvent_t handle (e.g. torch.cuda.Event(...).cuda_event); other positions stay NULL."""
+    arr = (ctypes.c_void_p * (2 * MOE_NUM_STAGES))()
+    for i, h in events.items():
+        arr[i] = h
+    return arr
 
 
 def moe_route(dims: Dims, x, w_gate, topk_idx, topk_w, logits=None, gate_bias=None, stream=None):
@@ -128,13 +148,19 @@ def moe_combine(dims: Dims, y_perm, token_row, topk_w, y, y_dtype=None, accumula
                              _ptr(y), _stream(stream)))
 
 
+def moe_pack_weights(dims: Dims, which: int, w, w_packed, stream=None):
+    _check(lib().moe_pack_weights(ctypes.byref(dims.c()), which, _ptr(w), _ptr(w_packed), _stream(stream)))
+
+
 def moe_workspace_bytes(dims: Dims) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(dims.c())))
 
 
 def moe_forward(dims: Dims, x, w_gate, w1, w3, w2, y, workspace, gate_bias=None, y_dtype=None, accumulate=False,
-                stream=None, workspace_bytes=None):
-    o = _opts(gate_bias, y_dtype, accumulate, dims.dtype)
+                stream=None, workspace_bytes=None, stage_events=None):
+    """stage_events: None or the result of stage_event_array() (kept alive by the caller)."""
+    o = _opts(gate_bias, y_dtype, accumulate, dims.dtype,
+              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p).value)
     nbytes = workspace_bytes if workspace_bytes is not None else (
         workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
     _check(lib().moe_forward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),

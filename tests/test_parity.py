@@ -27,8 +27,9 @@ def M():
     return moe
 
 
-def dims_of(M, w, T=None):
-    return M.Dims(w.T if T is None else T, w.d, w.F, w.E, w.K, M.MOE_BF16 if w.dtype == "bf16" else M.MOE_F32)
+def dims_of(M, w, T=None, layout=0):
+    return M.Dims(w.T if T is None else T, w.d, w.F, w.E, w.K, M.MOE_BF16 if w.dtype == "bf16" else M.MOE_F32,
+                  layout)
 
 
 SMALL = {
@@ -68,7 +69,7 @@ def gpu_route(M, L, T=None):
 
 def gpu_forward(M, L, accumulate=False, y0=None, y_dtype=None):
     w = L.w
-    dm = dims_of(M, w)
+    dm = dims_of(M, w, layout=M.MOE_LAYOUT_PACKED if getattr(L, "packed", False) else M.MOE_LAYOUT_ROWMAJOR)
     ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
     if accumulate:
         y = dev(y0.astype(np.float32))
@@ -235,3 +236,91 @@ def test_forward_decode_full(M):
     ol, oi, ow = oracle.route(L.x, L.W["w_gate"], w.K)
     check_routing(w, gi, gw, gl, ol, oi, ow)
     check_forward(M, L)
+
+
+# ---------------------------------------------------------------- fragment-packed weights
+
+def pack(M, w, arr, which):
+    """Pack one weight tensor on the GPU (torch tensor in, torch tensor out)."""
+    dm = dims_of(M, w)
+    out = torch.empty_like(arr)
+    M.moe_pack_weights(dm, which, arr, out)
+    return out
+
+
+def test_pack_is_the_documented_permutation(M):
+    """Unique ids through moe_pack_weights land where the layout definition in moe.h puts them."""
+    E, N, K = 3, 64, 128
+    for dtype, V in (("f32", 4), ("bf16", 8)):
+        say(f"[pack] {dtype} E={E} N={N} K={K}")
+        ids = np.arange(E * N * K, dtype=np.int64)
+        if dtype == "f32":
+            w = ids.astype(np.float32).reshape(E, N, K)
+        else:   # bf16 holds exact integers only up to 256: use the raw 16-bit patterns as ids
+            w = (ids % 65536).astype(np.uint16).reshape(E, N, K)
+        wk = mi.Workload("pk", T=1, d=K, F=N, E=E, dtype=dtype)
+        got = host(pack(M, wk, dev(w), M.MOE_W_UP)).reshape(-1)
+        assert sorted(got.tolist()) == sorted(w.reshape(-1).tolist())          # a permutation
+        e, n, k = np.meshgrid(np.arange(E), np.arange(N), np.arange(K), indexing="ij")
+        lane = n % 16 + 16 * ((k // V) % 4)
+        pos = ((e * (N // 16) + n // 16) * (K // (4 * V)) + k // (4 * V)) * 64 * V + lane * V + k % V
+        assert np.array_equal(got[pos.reshape(-1)], w.reshape(-1))
+
+
+def packed_layer(M, L):
+    w = L.w
+    dW = dict(L.dW)
+    dW["w1"] = pack(M, w, L.dW["w1"], M.MOE_W_UP)
+    dW["w3"] = pack(M, w, L.dW["w3"], M.MOE_W_UP)
+    dW["w2"] = pack(M, w, L.dW["w2"], M.MOE_W_DOWN)
+    P = Layer.__new__(Layer)
+    P.__dict__.update(L.__dict__)
+    P.dW = dW
+    P.packed = True
+    return P
+
+
+def forward_with_layout(M, L, layout):
+    w = L.w
+    dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16 if w.dtype == "bf16" else M.MOE_F32, layout)
+    ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device="cuda")
+    M.moe_forward(dm, L.dx, L.dW["w_gate"], L.dW["w1"], L.dW["w3"], L.dW["w2"], y, ws, gate_bias=L.dbias)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "ragged_f32", "ragged_bf16_d192", "skew_small_bf16",
+                                  "e16_k4_bf16", "e64_k8_f32"])
+def test_packed_forward_bit_identical_and_in_tolerance(M, name):
+    w = SMALL[name]
+    say(f"[packed] {name}")
+    L = Layer(w)
+    y_row = forward_with_layout(M, L, M.MOE_LAYOUT_ROWMAJOR)
+    y_pk = forward_with_layout(M, packed_layer(M, L), M.MOE_LAYOUT_PACKED)
+    assert np.array_equal(y_row, y_pk)
+    r = oracle.forward(L.x, L.W["w_gate"], L.W["w1"], L.W["w3"], L.W["w2"], w.K, bias=L.W["bias"])
+    keep = gaps(r["logits"], w.K)[0] > TIE
+    assert rel_err(y_pk[keep], r["y"][keep]) <= tolerance(w.dtype)
+
+
+def test_packed_expert_ffn(M):
+    w = SMALL["ragged_bf16"]
+    say("[packed] moe_expert_ffn")
+    y, x_perm, offsets, W = expert_ffn_case(M, w, 1.5, 4242)
+    S = w.T * w.K
+    dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16, M.MOE_LAYOUT_PACKED)
+    h = torch.empty((S, w.F), dtype=torch.bfloat16, device="cuda")
+    yp = torch.empty((S, w.d), dtype=torch.float32, device="cuda")
+    M.moe_expert_ffn(dm, dev(x_perm), dev(offsets), pack(M, w, dev(W["w1"]), M.MOE_W_UP),
+                     pack(M, w, dev(W["w3"]), M.MOE_W_UP), pack(M, w, dev(W["w2"]), M.MOE_W_DOWN), h, yp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(yp), y)
+
+
+def test_forward_decode_full_packed(M):
+    """The decode step as the benchmark runs it (packed weights): all tokens against the oracle."""
+    w = mi.WORKLOADS["decode_T32"]
+    say(f"[packed] {w.name} (full size, all tokens)")
+    L = Layer(w)
+    check_forward(M, packed_layer(M, L))
