@@ -308,7 +308,9 @@ void launch_stream_l(int layout, const void* act, const int32_t* row_src, const 
 
 void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row_src, const int32_t* offsets,
                       int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream) {
-  if (dtype == kBF16)
+  if (tile_gemm_applies(dtype, rows, E, d, F))
+    launch_tile_up(layout, act, row_src, offsets, rows, d, F, E, w1, w3, h, stream);
+  else if (dtype == kBF16)
     launch_stream_l<bf16_t, true, bf16_t>(layout, act, row_src, offsets, rows, E, w1, w3, h, d, F, stream);
   else
     launch_stream_l<float, true, float>(layout, act, row_src, offsets, rows, E, w1, w3, h, d, F, stream);
@@ -316,7 +318,9 @@ void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row
 
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
                         int E, const void* w2, float* y_perm, hipStream_t stream) {
-  if (dtype == kBF16)
+  if (tile_gemm_applies(dtype, rows, E, d, F))
+    launch_tile_down(layout, h, offsets, rows, d, F, E, w2, y_perm, stream);
+  else if (dtype == kBF16)
     launch_stream_l<bf16_t, false, float>(layout, h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, stream);
   else
     launch_stream_l<float, false, float>(layout, h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, stream);

@@ -33,6 +33,14 @@ void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
                         int E, const void* w2, float* y_perm, hipStream_t stream);
 
+// Tiled (LDS-staged, 256 x 256) grouped GEMMs for large groups; tile_gemm_applies says when
+// they are used instead of the streaming kernels.
+bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F);
+void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
+                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
+                      const void* w2, float* y_perm, hipStream_t stream);
+
 // Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
 void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_packed, hipStream_t stream);
 

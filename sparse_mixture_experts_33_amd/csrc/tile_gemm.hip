@@ -1,0 +1,224 @@
+// Tiled grouped GEMM for large expert groups (prefill): the same two projections as the
+// streaming kernel (SwiGLU expert, xyznot.com summary "Método"; only routed rows exist, ja.news.hada.io
+// summary on zero-gate experts), shaped for the matrix cores instead of for the weight stream.
+//
+//   C[w][t] = sum_k W[w][k] * X[t][k]     (w: weight row = output column, t: token row of the group)
+//
+// Workgroup tile: BW weight rows x BT tokens (SwiGLU: BW/2 rows of w1 and the same BW/2 rows of
+// w3, so that silu(a)*b is formed in registers), k-steps of 64, two LDS stages. Four wavefronts
+// in a 2 x 2 arrangement, each BW/2 x BT/2 with 16x16x32 bf16 MFMAs accumulating in fp32.
+//
+// LDS holds both operands in matrix-core fragment order: a fragment is 16 rows x 32 k, 1 KB,
+// lane l holding row l%16 and k = 8*(l/16)..+7. Every global->LDS write and every LDS->register
+// read of a wavefront is then one contiguous 1 KB, free of bank conflicts for any bank count.
+// Weights in the packed layout arrive already in that order (1 KB contiguous global loads).
+//
+// Tiles are numbered expert-major, then weight tile, then token tile, so the token tiles that
+// share one weight tile are adjacent; the linear index is remapped so that adjacent tiles go to
+// workgroups on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps a
+// weight tile in that XCD's L2 while its token tiles run. Token rows past a group's end load a
+// valid row and are not stored. The k loop prefetches step s+1 into registers while step s is
+// multiplied out of LDS.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kXcds = 8;
+
+__device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
+
+template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
+__global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
+                                                           const int32_t* __restrict__ row_src,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const bf16_t* __restrict__ wa,
+                                                           const bf16_t* __restrict__ wb, OutT* __restrict__ out,
+                                                           int K, int N, int E) {
+  constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
+  constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
+  constexpr int TF = BT / 16 * 2;           // token fragments per k-step
+  constexpr int WL = WF / 4;                // weight fragment loads per wavefront per step
+  constexpr int TL = TF / 4;                // token fragment loads per wavefront per step
+  constexpr int AB = BW / 32;               // weight blocks per wavefront
+  constexpr int BB = BT / 32;               // token blocks per wavefront
+  constexpr int STAGE = (WF + TF) * 1024;   // bytes per LDS stage
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int32_t s_tile0[kMaxExperts + 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave >> 1, wt = wave & 1;
+
+  if (threadIdx.x <= E) s_off[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  const int NT = N / NW;
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      s_tile0[e] = acc;
+      acc += (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
+    }
+    s_tile0[E] = acc;
+  }
+  __syncthreads();
+  const int total = s_tile0[E];
+  const int Q = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  if (j >= Q) return;
+  const int tile = xcd * Q + j;
+  if (tile >= total) return;
+  int e = 0;
+  while (tile >= s_tile0[e + 1]) ++e;
+  const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
+  const int local = tile - s_tile0[e];
+  const int nt = local / mtiles, mt = local - nt * mtiles;
+  const int r0 = s_off[e] + mt * BT;
+  const int nrows = min(BT, s_off[e + 1] - r0);
+  const int n0 = nt * NW;
+
+  // This wavefront loads fragments g = wave + 4*i of each stage: 16-row block (wave>>1) + 2*i
+  // at the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
+  const int qh = wave & 1, b0 = wave >> 1;
+  const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // first element row of the tile's weights
+  const int w_lane = PACKED ? qh * 512 + lane * 8 : (lane & 15) * K + qh * 32 + (lane >> 4) * 8;
+  int32_t tsrc[TL];
+#pragma unroll
+  for (int i = 0; i < TL; ++i) {
+    const int rr = (b0 + 2 * i) * 16 + (lane & 15);
+    const int r = r0 + (rr < nrows ? rr : 0);
+    tsrc[i] = row_src ? row_src[r] : r;
+  }
+  const int t_lane = qh * 32 + (lane >> 4) * 8;
+  // k advance per step: packed weights move 2 fragments (1024 elements) per 16-row block
+  constexpr int64_t kWStep = PACKED ? 1024 : 64;
+
+  u32x4_t wreg[WL], treg[TL];
+  auto gload = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      int blk = b0 + 2 * i;
+      const bf16_t* w = wa;
+      if constexpr (SWIGLU) {
+        if (i >= WL / 2) {  // blocks BW/32.. hold w3 (b0 + 2i >= BW/32 exactly when i >= WL/2)
+          w = wb;
+          blk -= BW / 32;
+        }
+      }
+      wreg[i] = load16_nt(w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kWStep + w_lane);
+    }
+#pragma unroll
+    for (int i = 0; i < TL; ++i) treg[i] = load16(act + (int64_t)tsrc[i] * K + (int64_t)s * 64 + t_lane);
+  };
+  auto lstore = [&](int stage) {
+    uint8_t* base = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < WL; ++i) store16(base + (wave + 4 * i) * 1024 + lane * 16, wreg[i]);
+#pragma unroll
+    for (int i = 0; i < TL; ++i) store16(base + WF * 1024 + (wave + 4 * i) * 1024 + lane * 16, treg[i]);
+  };
+
+  f32x4_t acc[AB][BB];
+#pragma unroll
+  for (int a = 0; a < AB; ++a)
+#pragma unroll
+    for (int b = 0; b < BB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // weight block of the wavefront's a-th A fragment
+  auto wblock = [&](int a) -> int {
+    if constexpr (SWIGLU) return a < AB / 2 ? wr * (AB / 2) + a : BW / 32 + wr * (AB / 2) + (a - AB / 2);
+    else return wr * AB + a;
+  };
+
+  const int nsteps = K / 64;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nsteps) gload(s + 1);
+    const uint8_t* base = smem + cur * STAGE;
+#pragma unroll 1
+    for (int q = 0; q < 2; ++q) {
+      u32x4_t A[AB], B[BB];
+#pragma unroll
+      for (int a = 0; a < AB; ++a) A[a] = load16(base + (wblock(a) * 2 + q) * 1024 + lane * 16);
+#pragma unroll
+      for (int b = 0; b < BB; ++b) B[b] = load16(base + WF * 1024 + ((wt * BB + b) * 2 + q) * 1024 + lane * 16);
+#pragma unroll
+      for (int a = 0; a < AB; ++a)
+#pragma unroll
+        for (int b = 0; b < BB; ++b) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+    }
+    if (s + 1 < nsteps) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
+  const int li = lane & 15, lg = lane >> 4;
+  if constexpr (SWIGLU) {
+#pragma unroll
+    for (int a = 0; a < AB / 2; ++a)
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        const int tr = (wt * BB + b) * 16 + li;
+        if (tr >= nrows) continue;
+        const int f = n0 + (wr * (AB / 2) + a) * 16 + 4 * lg;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = silu_t(acc[a][b][q]) * acc[a + AB / 2][b][q];
+        *reinterpret_cast<u32x2_t*>(out + (int64_t)(r0 + tr) * N + f) =
+            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < AB; ++a)
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        const int tr = (wt * BB + b) * 16 + li;
+        if (tr >= nrows) continue;
+        const int n = n0 + (wr * AB + a) * 16 + 4 * lg;
+        store16(out + (int64_t)(r0 + tr) * N + n, u32x4_t{__float_as_uint(acc[a][b][0]), __float_as_uint(acc[a][b][1]),
+                                                          __float_as_uint(acc[a][b][2]), __float_as_uint(acc[a][b][3])});
+      }
+  }
+}
+
+template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
+void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
+                 const void* wb, void* out, int K, int N, hipStream_t s) {
+  constexpr int NW = SWIGLU ? BW / 2 : BW;
+  const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW);
+  const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
+                     static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E);
+}
+
+}  // namespace
+
+bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F) {
+  // bf16 only; large groups; shapes that the 256 x 256 tiles and 64-deep k-steps divide
+  return dtype == kBF16 && rows >= 128 * (int64_t)E && F % 128 == 0 && d % 256 == 0 && d % 64 == 0 && F % 64 == 0;
+}
+
+void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
+                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t s) {
+  if (layout == kPacked)
+    launch_tile<256, 256, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, s);
+  else
+    launch_tile<256, 256, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, s);
+}
+
+void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
+                      const void* w2, float* y_perm, hipStream_t s) {
+  if (layout == kPacked)
+    launch_tile<256, 256, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, s);
+  else
+    launch_tile<256, 256, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, s);
+}
+
+}  // namespace moe

@@ -324,3 +324,74 @@ def test_forward_decode_full_packed(M):
     say(f"[packed] {w.name} (full size, all tokens)")
     L = Layer(w)
     check_forward(M, packed_layer(M, L))
+
+
+# ---------------------------------------------------------------- tiled (large-group) path
+
+TILED = {
+    # expected rows per expert >= 128 and d % 256 == 0, F % 128 == 0: the LDS-tiled GEMMs run
+    "tile_e4": mi.Workload("tile_e4", T=700, d=256, F=512, E=4, K=2, dtype="bf16", seed=701),
+    "tile_e8": mi.Workload("tile_e8", T=1200, d=512, F=384, E=8, K=2, dtype="bf16", seed=702),
+    "tile_skew": mi.Workload("tile_skew", T=2000, d=256, F=256, E=8, K=2, dtype="bf16", skew_bias=True, seed=703),
+    "tile_k1": mi.Workload("tile_k1", T=1100, d=256, F=256, E=4, K=1, dtype="bf16", seed=704),
+}
+
+
+@pytest.mark.parametrize("name", list(TILED))
+def test_tiled_forward(M, name):
+    w = TILED[name]
+    say(f"[tiled] {name} T={w.T} d={w.d} F={w.F} E={w.E} K={w.K}")
+    L = Layer(w)
+    y_row = forward_with_layout(M, L, M.MOE_LAYOUT_ROWMAJOR)
+    y_pk = forward_with_layout(M, packed_layer(M, L), M.MOE_LAYOUT_PACKED)
+    assert np.array_equal(y_row, y_pk)
+    r = oracle.forward(L.x, L.W["w_gate"], L.W["w1"], L.W["w3"], L.W["w2"], w.K, bias=L.W["bias"])
+    keep = gaps(r["logits"], w.K)[0] > TIE
+    err = rel_err(y_pk[keep], r["y"][keep])
+    say(f"  max|d|/max|ref| = {err:.3e} over {keep.sum()} tokens")
+    assert err <= tolerance(w.dtype)
+
+
+def test_tiled_expert_ffn_all_rows(M):
+    """moe_expert_ffn on the tiled path: every permuted row against the oracle."""
+    w = TILED["tile_e8"]
+    say("[tiled] moe_expert_ffn, all rows")
+    y, x_perm, offsets, W = expert_ffn_case(M, w, 2.0, 7001)
+    ref = oracle.expert_ffn(x_perm, offsets, W["w1"], W["w3"], W["w2"])
+    err = rel_err(y, ref)
+    say(f"  max|d|/max|ref| = {err:.3e}")
+    assert err <= tolerance(w.dtype)
+
+
+def sampled_tokens(idx, T, E, per_expert=6, extra=12, seed=0):
+    """Tokens for a sampled oracle check: the first and last tokens, and `per_expert` tokens routed
+    to each expert (all of them if fewer), drawn with a fixed seed."""
+    rng = np.random.default_rng(seed)
+    pick = {0, 1, T - 2, T - 1}
+    for e in range(E):
+        cand = np.flatnonzero((idx == e).any(1))
+        if len(cand):
+            pick.update(rng.choice(cand, size=min(per_expert, len(cand)), replace=False).tolist())
+    pick.update(rng.choice(T, size=extra, replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["prefill_T4096", "skewed_T16384"])
+def test_forward_full_size_sampled(M, name):
+    """Full-size Mixtral layers in the benchmark's configuration (packed weights), checked on a
+    sample of tokens (the oracle computes tokens independently, so a sample is exact)."""
+    w = mi.WORKLOADS[name]
+    say(f"[full] {name}: T={w.T} packed weights")
+    L = packed_layer(M, Layer(w))
+    gi, gw, gl = gpu_route(M, L)
+    ol, oi, ow = oracle.route(L.x, L.W["w_gate"], w.K, bias=L.W["bias"])
+    check_routing(w, gi, gw, gl, ol, oi, ow)
+    counts = np.bincount(oi.ravel(), minlength=w.E)
+    say(f"  tokens per expert: {counts.tolist()}")
+    y = gpu_forward(M, L)
+    tok = sampled_tokens(oi, w.T, w.E, seed=w.seed)
+    r = oracle.forward(L.x, L.W["w_gate"], L.W["w1"], L.W["w3"], L.W["w2"], w.K, bias=L.W["bias"], tokens=tok)
+    keep = gaps(r["logits"], w.K)[0] > TIE
+    err = rel_err(y[tok][keep], r["y"][keep])
+    say(f"  max|d|/max|ref| = {err:.3e} over {keep.sum()} sampled tokens")
+    assert err <= tolerance(w.dtype)
