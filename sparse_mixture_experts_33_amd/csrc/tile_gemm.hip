@@ -5,8 +5,9 @@
 //   C[w][t] = sum_k W[w][k] * X[t][k]     (w: weight row = output column, t: token row of the group)
 //
 // Workgroup tile: BW weight rows x BT tokens (SwiGLU: BW/2 rows of w1 and the same BW/2 rows of
-// w3, so that silu(a)*b is formed in registers), k-steps of 64, two LDS stages. Four wavefronts
-// in a 2 x 2 arrangement, each BW/2 x BT/2 with 16x16x32 bf16 MFMAs accumulating in fp32.
+// w3, so that silu(a)*b is formed in registers), k-steps of 64, two LDS stages. Eight wavefronts
+// (two per SIMD, so one's LDS and memory waits overlap the other's MFMAs) in a 2 x 4
+// arrangement, each BW/2 weight rows x BT/4 tokens, 16x16x32 bf16 MFMAs accumulating in fp32.
 //
 // LDS holds both operands in matrix-core fragment order: a fragment is 16 rows x 32 k, 1 KB,
 // lane l holding row l%16 and k = 8*(l/16)..+7. Every global->LDS write and every LDS->register
@@ -30,7 +31,7 @@ constexpr int kXcds = 8;
 __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 
 template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
-__global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
+__global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
                                                            const int32_t* __restrict__ offsets,
                                                            const bf16_t* __restrict__ wa,
@@ -39,10 +40,11 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restr
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
   constexpr int TF = BT / 16 * 2;           // token fragments per k-step
-  constexpr int WL = WF / 4;                // weight fragment loads per wavefront per step
-  constexpr int TL = TF / 4;                // token fragment loads per wavefront per step
+  constexpr int NWV = 8;                    // wavefronts: 2 over weight rows x 4 over tokens
+  constexpr int WL = WF / NWV;              // weight fragment loads per wavefront per step
+  constexpr int TL = TF / NWV;              // token fragment loads per wavefront per step
   constexpr int AB = BW / 32;               // weight blocks per wavefront
-  constexpr int BB = BT / 32;               // token blocks per wavefront
+  constexpr int BB = BT / 64;               // token blocks per wavefront
   constexpr int STAGE = (WF + TF) * 1024;   // bytes per LDS stage
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restr
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wr = wave >> 1, wt = wave & 1;
+  const int wr = wave >> 2, wt = wave & 3;
 
   if (threadIdx.x <= E) s_off[threadIdx.x] = offsets[threadIdx.x];
   __syncthreads();
@@ -80,15 +82,15 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restr
   const int nrows = min(BT, s_off[e + 1] - r0);
   const int n0 = nt * NW;
 
-  // This wavefront loads fragments g = wave + 4*i of each stage: 16-row block (wave>>1) + 2*i
-  // at the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
+  // This wavefront loads fragments g = wave + 8*i of each stage: 16-row block (wave>>1) + 4*i at
+  // the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
   const int qh = wave & 1, b0 = wave >> 1;
   const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // first element row of the tile's weights
   const int w_lane = PACKED ? qh * 512 + lane * 8 : (lane & 15) * K + qh * 32 + (lane >> 4) * 8;
   int32_t tsrc[TL];
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    const int rr = (b0 + 2 * i) * 16 + (lane & 15);
+    const int rr = (b0 + 4 * i) * 16 + (lane & 15);
     const int r = r0 + (rr < nrows ? rr : 0);
     tsrc[i] = row_src ? row_src[r] : r;
   }
@@ -100,10 +102,10 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restr
   auto gload = [&](int s) {
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
-      int blk = b0 + 2 * i;
+      int blk = b0 + 4 * i;
       const bf16_t* w = wa;
       if constexpr (SWIGLU) {
-        if (i >= WL / 2) {  // blocks BW/32.. hold w3 (b0 + 2i >= BW/32 exactly when i >= WL/2)
+        if (i >= WL / 2) {  // blocks BW/32.. hold w3 (b0 + 4i >= BW/32 exactly when i >= WL/2)
           w = wb;
           blk -= BW / 32;
         }
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(const bf16_t* __restr
   auto lstore = [&](int stage) {
     uint8_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < WL; ++i) store16(base + (wave + 4 * i) * 1024 + lane * 16, wreg[i]);
+    for (int i = 0; i < WL; ++i) store16(base + (wave + 8 * i) * 1024 + lane * 16, wreg[i]);
 #pragma unroll
-    for (int i = 0; i < TL; ++i) store16(base + WF * 1024 + (wave + 4 * i) * 1024 + lane * 16, treg[i]);
+    for (int i = 0; i < TL; ++i) store16(base + WF * 1024 + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
   };
 
   f32x4_t acc[AB][BB];
@@ -193,7 +195,7 @@ void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW);
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(256), 0, s,
+  hipLaunchKernelGGL((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                      static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
                      static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E);
 }
