@@ -70,7 +70,8 @@ size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, h, y_perm, total;
+  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, h, y_perm, y_part, total;
+  int ksplit;  // k-ranges of the down projection (partials 1.. live at y_part)
 };
 
 Workspace layout(const moe_dims& m) {
@@ -85,6 +86,8 @@ Workspace layout(const moe_dims& m) {
   w.token_row = o; o = align256(o + S * 4);
   w.h = o;         o = align256(o + S * (size_t)m.F * elem_bytes(m.dtype));
   w.y_perm = o;    o = align256(o + S * (size_t)m.d * 4);
+  w.ksplit = moe::tile_down_ksplit(m.dtype, (int64_t)S, m.E, m.d, m.F);
+  w.y_part = o;    o = align256(o + (size_t)(w.ksplit - 1) * S * (size_t)m.d * 4);
   w.total = o;
   return w;
 }
@@ -175,7 +178,8 @@ moe_status moe_expert_ffn(const moe_dims* dims, const void* x_perm, const int32_
   moe::launch_expert_up(m.dtype, m.weight_layout, x_perm, nullptr, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h_ws,
                         s);
   MOE_TRY(check_launch("moe_expert_ffn (up)"));
-  moe::launch_expert_down(m.dtype, m.weight_layout, h_ws, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, s);
+  moe::launch_expert_down(m.dtype, m.weight_layout, h_ws, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, 1, nullptr,
+                          s);
   return check_launch("moe_expert_ffn (down)");
 }
 
@@ -190,7 +194,7 @@ moe_status moe_combine(const moe_dims* dims, const moe_opts* opts, const float* 
   int yd = 0;
   MOE_TRY(check_opts(m, opts, &yd));
   if (m.T == 0) return MOE_OK;
-  moe::launch_combine(y_perm, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y,
+  moe::launch_combine(y_perm, nullptr, 0, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y,
                       static_cast<hipStream_t>(stream));
   return check_launch("moe_combine");
 }
@@ -249,6 +253,7 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   int32_t* token_row = reinterpret_cast<int32_t*>(ws + L.token_row);
   void* h = ws + L.h;
   float* y_perm = reinterpret_cast<float*>(ws + L.y_perm);
+  float* y_part = reinterpret_cast<float*>(ws + L.y_part);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   void* const* ev = opts ? opts->stage_events : nullptr;
@@ -272,11 +277,13 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   MOE_TRY(check_launch("moe_forward (expert up)"));
   MOE_TRY(mark(2 * MOE_STAGE_EXPERT_UP + 1));
   MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN));
-  moe::launch_expert_down(m.dtype, m.weight_layout, h, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, s);
+  moe::launch_expert_down(m.dtype, m.weight_layout, h, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, L.ksplit, y_part,
+                          s);
   MOE_TRY(check_launch("moe_forward (expert down)"));
   MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN + 1));
   MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
-  moe::launch_combine(y_perm, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0, y, s);
+  moe::launch_combine(y_perm, y_part, L.ksplit - 1, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0,
+                      y, s);
   MOE_TRY(check_launch("moe_forward (combine)"));
   return mark(2 * MOE_STAGE_COMBINE + 1);
 }

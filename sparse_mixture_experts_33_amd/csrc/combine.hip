@@ -2,8 +2,10 @@
 // section 1; xyznot.com summary, "Método"): the expert outputs return to their original token
 // positions (zh.newsflash.city article, expert-parallel paragraph) and are added.
 //
-// One wavefront (or, for few tokens, one workgroup) per token, 16-byte accesses along d. The K terms are added in fp32 in slot
-// order, s = w0*o0, then s = fma(w_k, o_k, s), so the result does not depend on scheduling.
+// One wavefront (or, for few tokens, one workgroup) per token, 16-byte accesses along d. When the
+// down projection was split along k, an expert output is first rebuilt as the sum of its k-range
+// partials in range order. The K terms are then added in fp32 in slot order, s = w0*o0, then
+// s = fma(w_k, o_k, s), so the result does not depend on scheduling.
 // HBM-bound: T*K*d*4 bytes read, T*d*|y| written (plus T*d*4 read when accumulating).
 //
 // Also the RMSNorm of a residual stream for stacks of such layers (the pages describe no norm;
@@ -19,6 +21,7 @@ namespace {
 // once) for few tokens.
 template <int MODE, int TPB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const float* __restrict__ y_part, int nparts,
                                                       const int32_t* __restrict__ token_row,
                                                       const float* __restrict__ topk_w, int64_t T, int d, int K,
                                                       void* __restrict__ y) {
@@ -33,12 +36,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     rows[k] = (k < K) ? token_row[t * K + k] : 0;
     g[k] = (k < K) ? topk_w[t * K + k] : 0.0f;
   }
+  const int64_t part_stride = (int64_t)T * K * d;
+  // expert output of slot k: y_perm row plus the partial sums of the other k-ranges, in order
+  auto expert_out = [&](int k, int c) {
+    const int64_t off = (int64_t)rows[k] * d + c;
+    f32x4_t o = *reinterpret_cast<const f32x4_t*>(y_perm + off);
+    for (int p = 0; p < nparts; ++p) o = o + *reinterpret_cast<const f32x4_t*>(y_part + p * part_stride + off);
+    return o;
+  };
   for (int c = lt * 4; c < d; c += NT * 4) {
-    f32x4_t s = g[0] * *reinterpret_cast<const f32x4_t*>(y_perm + (int64_t)rows[0] * d + c);
+    f32x4_t s = g[0] * expert_out(0, c);
 #pragma unroll
     for (int k = 1; k < kMaxTopK; ++k) {
       if (k < K) {
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(y_perm + (int64_t)rows[k] * d + c);
+        const f32x4_t o = expert_out(k, c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) s[q] = fmaf(g[k], o[q], s[q]);
       }
@@ -56,14 +67,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 template <int MODE>
-void launch_mode(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K, void* y,
-                 hipStream_t stream) {
+void launch_mode(const float* y_perm, const float* y_part, int nparts, const int32_t* token_row, const float* topk_w,
+                 int64_t T, int d, int K, void* y, hipStream_t stream) {
   if (T <= 1024) {
-    hipLaunchKernelGGL((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, token_row, topk_w,
-                       T, d, K, y);
-  } else {
-    hipLaunchKernelGGL((combine_kernel<MODE, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, y_perm,
+    hipLaunchKernelGGL((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, y_part, nparts,
                        token_row, topk_w, T, d, K, y);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<MODE, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, y_perm, y_part,
+                       nparts, token_row, topk_w, T, d, K, y);
   }
 }
 
@@ -92,14 +103,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 }  // namespace
 
-void launch_combine(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K,
-                    int y_dtype, int accumulate, void* y, hipStream_t stream) {
+void launch_combine(const float* y_perm, const float* y_part, int nparts, const int32_t* token_row, const float* topk_w,
+                    int64_t T, int d, int K, int y_dtype, int accumulate, void* y, hipStream_t stream) {
   if (accumulate)
-    launch_mode<2>(y_perm, token_row, topk_w, T, d, K, y, stream);
+    launch_mode<2>(y_perm, y_part, nparts, token_row, topk_w, T, d, K, y, stream);
   else if (y_dtype == kBF16)
-    launch_mode<1>(y_perm, token_row, topk_w, T, d, K, y, stream);
+    launch_mode<1>(y_perm, y_part, nparts, token_row, topk_w, T, d, K, y, stream);
   else
-    launch_mode<0>(y_perm, token_row, topk_w, T, d, K, y, stream);
+    launch_mode<0>(y_perm, y_part, nparts, token_row, topk_w, T, d, K, y, stream);
 }
 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream) {

@@ -317,9 +317,9 @@ void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row
 }
 
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
-                        int E, const void* w2, float* y_perm, hipStream_t stream) {
+                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream) {
   if (tile_gemm_applies(dtype, rows, E, d, F))
-    launch_tile_down(layout, h, offsets, rows, d, F, E, w2, y_perm, stream);
+    launch_tile_down(layout, h, offsets, rows, d, F, E, w2, y_perm, ksplit, y_part, stream);
   else if (dtype == kBF16)
     launch_stream_l<bf16_t, false, float>(layout, h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, stream);
   else

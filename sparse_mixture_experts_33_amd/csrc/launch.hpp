@@ -12,6 +12,7 @@ constexpr int kRowMajor = 0;
 constexpr int kPacked = 1;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 64;
+constexpr int kMaxKSplit = 4;  // k-ranges of the down projection in moe_forward
 
 void launch_route(int dtype, const void* x, const void* w_gate, const float* bias, int64_t T, int d, int E, int K,
                   int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream);
@@ -30,22 +31,27 @@ void launch_gather_rows(const void* x, const int32_t* row_token, int64_t rows, i
 // layout: kRowMajor or kPacked (fragment-packed weights, see moe_pack_weights in moe.h).
 void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row_src, const int32_t* offsets,
                       int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+// ksplit > 1 (moe_forward only, tiled path only): k-range p > 0 writes its partial sums to
+// y_part + (p-1)*rows*d; y_perm then holds only range 0 and the combine adds the rest.
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
-                        int E, const void* w2, float* y_perm, hipStream_t stream);
+                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
 // Tiled (LDS-staged, 256 x 256) grouped GEMMs for large groups; tile_gemm_applies says when
 // they are used instead of the streaming kernels.
 bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F);
+// k-ranges the down projection of moe_forward is split into (1 = no split).
+int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F);
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
-                      const void* w2, float* y_perm, hipStream_t stream);
+                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
 // Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
 void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_packed, hipStream_t stream);
 
-void launch_combine(const float* y_perm, const int32_t* token_row, const float* topk_w, int64_t T, int d, int K,
-                    int y_dtype, int accumulate, void* y, hipStream_t stream);
+// nparts extra partial-sum buffers (y_part, each rows*d) are added to y_perm in order first.
+void launch_combine(const float* y_perm, const float* y_part, int nparts, const int32_t* token_row, const float* topk_w,
+                    int64_t T, int d, int K, int y_dtype, int accumulate, void* y, hipStream_t stream);
 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream);
 

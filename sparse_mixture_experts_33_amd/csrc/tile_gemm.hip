@@ -23,6 +23,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <cmath>
+
 namespace moe {
 namespace {
 
@@ -36,7 +38,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            const int32_t* __restrict__ offsets,
                                                            const bf16_t* __restrict__ wa,
                                                            const bf16_t* __restrict__ wb, OutT* __restrict__ out,
-                                                           int K, int N, int E) {
+                                                           int K, int N, int E, int ksplit, float* __restrict__ part,
+                                                           int64_t part_stride) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
   constexpr int TF = BT / 16 * 2;           // token fragments per k-step
@@ -67,12 +70,16 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     s_tile0[E] = acc;
   }
   __syncthreads();
+  // Split-K (down projection only): every tile is computed as `ksplit` independent k-ranges;
+  // range p > 0 writes its partial sums to part + (p-1)*part_stride, to be added in a fixed
+  // order by the consumer.
   const int total = s_tile0[E];
-  const int Q = (total + kXcds - 1) / kXcds;
+  const int Q = (total * ksplit + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   if (j >= Q) return;
-  const int tile = xcd * Q + j;
-  if (tile >= total) return;
+  const int tsplit = xcd * Q + j;
+  if (tsplit >= total * ksplit) return;
+  const int p = tsplit / total, tile = tsplit - p * total;
   int e = 0;
   while (tile >= s_tile0[e + 1]) ++e;
   const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
@@ -81,6 +88,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   const int r0 = s_off[e] + mt * BT;
   const int nrows = min(BT, s_off[e + 1] - r0);
   const int n0 = nt * NW;
+  if constexpr (!SWIGLU) {
+    if (p > 0) out = reinterpret_cast<OutT*>(part + (int64_t)(p - 1) * part_stride);
+  }
 
   // This wavefront loads fragments g = wave + 8*i of each stage: 16-row block (wave>>1) + 4*i at
   // the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
@@ -135,13 +145,14 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     else return wr * AB + a;
   };
 
-  const int nsteps = K / 64;
-  gload(0);
+  const int nsteps_all = K / 64;
+  const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
+  gload(s_lo);
   lstore(0);
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+  for (int s = s_lo; s < s_hi; ++s) {
+    const int cur = (s - s_lo) & 1;
+    if (s + 1 < s_hi) gload(s + 1);
     const uint8_t* base = smem + cur * STAGE;
 #pragma unroll 1
     for (int q = 0; q < 2; ++q) {
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 #pragma unroll
         for (int b = 0; b < BB; ++b) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
     }
-    if (s + 1 < nsteps) lstore(cur ^ 1);
+    if (s + 1 < s_hi) lstore(cur ^ 1);
     __syncthreads();
   }
 
@@ -191,36 +202,61 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
 template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
 void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
-                 const void* wb, void* out, int K, int N, hipStream_t s) {
+                 const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;
-  const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW);
+  const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                      static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
-                     static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E);
+                     static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N);
 }
 
 }  // namespace
 
 bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F) {
   // bf16 only; large groups; shapes that the 256 x 256 tiles and 64-deep k-steps divide
-  return dtype == kBF16 && rows >= 128 * (int64_t)E && F % 128 == 0 && d % 256 == 0 && d % 64 == 0 && F % 64 == 0;
+  return dtype == kBF16 && rows >= 128 * (int64_t)E && F % 128 == 0 && d % 256 == 0 && F % 64 == 0;
+}
+
+int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
+  if (!tile_gemm_applies(dtype, rows, E, d, F)) return 1;
+  // Expected tiles of the down projection (a group of n rows takes n/256 + 1/2 token tiles on
+  // average), spread over 256 CUs in rounds of one tile per CU. A split into ks k-ranges turns
+  // each round into 1/ks of a round; every extra range costs one more fp32 partial written and
+  // read back (8*rows*d bytes at ~6.5 TB/s), expressed in tile times (a 256 x 256 x F tile at
+  // ~4 TFLOP/s per CU). The split depends on the sizes only, so the workspace size does too.
+  const double per_e = (double)rows / E;
+  const double tiles = (double)E * (per_e / 256.0 + 0.5) * (d / 256);
+  const double tile_s = 2.0 * 256 * 256 * (double)F / 4.0e12;
+  const double part_s = 8.0 * (double)rows * d / 6.5e12;
+  int best = 1;
+  double best_t = 1e30;
+  for (int ks = 1; ks <= kMaxKSplit && F / 64 >= 8 * ks; ++ks) {
+    const double t = std::ceil(tiles * ks / 256.0) / ks + (ks - 1) * part_s / tile_s;
+    if (t < best_t) {
+      best_t = t;
+      best = ks;
+    }
+  }
+  return best;
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, s);
+    launch_tile<256, 256, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
   else
-    launch_tile<256, 256, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, s);
+    launch_tile<256, 256, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
-                      const void* w2, float* y_perm, hipStream_t s) {
+                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, s);
+    launch_tile<256, 256, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit, y_part,
+                                             s);
   else
-    launch_tile<256, 256, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, s);
+    launch_tile<256, 256, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit, y_part,
+                                              s);
 }
 
 }  // namespace moe

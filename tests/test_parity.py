@@ -334,6 +334,8 @@ TILED = {
     "tile_e8": mi.Workload("tile_e8", T=1200, d=512, F=384, E=8, K=2, dtype="bf16", seed=702),
     "tile_skew": mi.Workload("tile_skew", T=2000, d=256, F=256, E=8, K=2, dtype="bf16", skew_bias=True, seed=703),
     "tile_k1": mi.Workload("tile_k1", T=1100, d=256, F=256, E=4, K=1, dtype="bf16", seed=704),
+    # F = 2048 lets moe_forward split the down projection into k-ranges summed in the combine
+    "tile_splitk": mi.Workload("tile_splitk", T=700, d=256, F=2048, E=4, K=2, dtype="bf16", seed=705),
 }
 
 
