@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int p = 0; p < nparts; ++p) o = o + *reinterpret_cast<const f32x4_t*>(y_part + p * part_stride + off);
     return o;
   };
+#pragma unroll 4
   for (int c = lt * 4; c < d; c += NT * 4) {
     f32x4_t s = g[0] * expert_out(0, c);
 #pragma unroll

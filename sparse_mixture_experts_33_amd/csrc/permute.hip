@@ -96,8 +96,10 @@ void launch_index(const int32_t* idx, int64_t S, int K, int E, int32_t* counts, 
 void launch_permute_index(const int32_t* topk_idx, int64_t T, int E, int K, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t stream) {
   const int64_t S = T * K;
-  // the LDS table holds E*NT int32 (32 KB)
-  if (E <= 8)
+  // the LDS table holds E*NT int32 (at most 32 KB); a single wavefront for few slots (decode)
+  if (S <= 512)
+    launch_index<64>(topk_idx, S, K, E, counts, offsets, row_token, token_row, stream);
+  else if (E <= 8)
     launch_index<1024>(topk_idx, S, K, E, counts, offsets, row_token, token_row, stream);
   else if (E <= 16)
     launch_index<512>(topk_idx, S, K, E, counts, offsets, row_token, token_row, stream);

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(256) void route_token_kernel(const T* __restrict__ 
   float acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
+#pragma unroll 4
   for (int k0 = threadIdx.x * V; k0 < d; k0 += 256 * V) {
     float xv[V];
     unpack16<T, V>(load16(x + t * d + k0), xv);
