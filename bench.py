@@ -57,25 +57,27 @@ def copy_probe():
     print(json.dumps({"probe": "copy", "bytes_per_copy": n, "copies": 3}), flush=True)
 
 
-def source_digest() -> str:
-    """sha256 of the kernel sources (a counter summary is only valid for the source it was taken on)."""
+def source_digest(files) -> str:
+    """sha256 (first 16 hex digits) of the named kernel sources, in the order given: a counter summary
+    is only valid for the source it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mixture_experts_33_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on this source."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if taken on the current source
+    of the files that define the kernel (listed in the summary as `source_files:`)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
+    f = re.search(r"source_files:\s*([^\n]+)", txt)
     m = re.search(r"source_digest:\s*(\w+)", txt)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not b or m.group(1) != source_digest():
+    if not f or not m or not b or m.group(1) != source_digest(f.group(1).split()):
         return None
     return float(b.group(1))
 

@@ -17,13 +17,22 @@
 // Tiles are numbered expert-major, then weight tile, then token tile, so the token tiles that
 // share one weight tile are adjacent; the linear index is remapped so that adjacent tiles go to
 // workgroups on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps a
-// weight tile in that XCD's L2 while its token tiles run. Token rows past a group's end load a
-// valid row and are not stored. The k loop prefetches step s+1 into registers while step s is
-// multiplied out of LDS.
+// weight tile in that XCD's L2 while its token tiles run.
+//
+// Token blocks (16 rows) are dealt to the four token wavefronts round-robin (wavefront t owns
+// blocks t, t+4, t+8, t+12), so the partly filled last tile of a group spreads its rows over the
+// SIMDs; a wavefront skips the MFMAs (and fragment reads) of blocks that lie wholly past the
+// group's end. Token rows past the end still load a valid row and are never stored.
+//
+// k loop, per step s: write step s+1 (loaded into registers during step s-1) to the free LDS
+// stage, load step s+2 into registers, multiply step s out of LDS, barrier. Writing at the start
+// of the step, not just before the barrier, lets the LDS writes complete under the MFMAs instead
+// of holding every wavefront at the barrier.
 #include "common.hpp"
 #include "launch.hpp"
 
 #include <cmath>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -85,8 +94,10 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
   const int local = tile - s_tile0[e];
   const int nt = local / mtiles, mt = local - nt * mtiles;
-  const int r0 = s_off[e] + mt * BT;
-  const int nrows = min(BT, s_off[e + 1] - r0);
+  const int r0 = __builtin_amdgcn_readfirstlane(s_off[e] + mt * BT);
+  const int nrows = __builtin_amdgcn_readfirstlane(min(BT, s_off[e + 1] - r0));
+  // token blocks of this wavefront that hold at least one row of the group
+  const int nbv = min(BB, max(0, ((nrows + 15) / 16 - wt + 3) / 4));
   const int n0 = nt * NW;
   if constexpr (!SWIGLU) {
     if (p > 0) out = reinterpret_cast<OutT*>(part + (int64_t)(p - 1) * part_stride);
@@ -145,30 +156,58 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     else return wr * AB + a;
   };
 
-  const int nsteps_all = K / 64;
-  const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
-  gload(s_lo);
-  lstore(0);
-  __syncthreads();
-  for (int s = s_lo; s < s_hi; ++s) {
-    const int cur = (s - s_lo) & 1;
-    if (s + 1 < s_hi) gload(s + 1);
-    const uint8_t* base = smem + cur * STAGE;
+  // Token fragment of the wavefront's b-th token block (block wt + 4b) at k-half q.
+  auto tfrag = [&](const uint8_t* base, int b, int q) {
+    return load16(base + WF * 1024 + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
+  };
+  // Multiply one LDS stage. FULL: all BB token blocks of the wavefront hold rows; otherwise only
+  // the first nbv do (the last, partly filled tile of a group).
+  auto compute = [&](const uint8_t* base, auto full) {
 #pragma unroll 1
     for (int q = 0; q < 2; ++q) {
-      u32x4_t A[AB], B[BB];
+      u32x4_t A[AB];
 #pragma unroll
       for (int a = 0; a < AB; ++a) A[a] = load16(base + (wblock(a) * 2 + q) * 1024 + lane * 16);
+      if constexpr (decltype(full)::value) {
+        u32x4_t B[BB];
 #pragma unroll
-      for (int b = 0; b < BB; ++b) B[b] = load16(base + WF * 1024 + ((wt * BB + b) * 2 + q) * 1024 + lane * 16);
+        for (int b = 0; b < BB; ++b) B[b] = tfrag(base, b, q);
 #pragma unroll
-      for (int a = 0; a < AB; ++a)
+        for (int a = 0; a < AB; ++a)
 #pragma unroll
-        for (int b = 0; b < BB; ++b) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+          for (int b = 0; b < BB; ++b) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < BB; ++b) {
+          if (b < nbv) {
+            const u32x4_t Bb = tfrag(base, b, q);
+#pragma unroll
+            for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], Bb, acc[a][b]);
+          }
+        }
+      }
     }
-    if (s + 1 < s_hi) lstore(cur ^ 1);
+  };
+
+  const int nsteps_all = K / 64;
+  const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
+  auto kloop = [&](auto full) {
+    gload(s_lo);
+    lstore(0);
+    if (s_lo + 1 < s_hi) gload(s_lo + 1);
     __syncthreads();
-  }
+    for (int s = s_lo; s < s_hi; ++s) {
+      const int cur = (s - s_lo) & 1;
+      if (s + 1 < s_hi) lstore(cur ^ 1);
+      if (s + 2 < s_hi) gload(s + 2);
+      if (decltype(full)::value || nbv > 0) compute(smem + cur * STAGE, full);
+      __syncthreads();
+    }
+  };
+  if (nbv == BB)
+    kloop(std::true_type{});
+  else
+    kloop(std::false_type{});
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
   const int li = lane & 15, lg = lane >> 4;
@@ -177,7 +216,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     for (int a = 0; a < AB / 2; ++a)
 #pragma unroll
       for (int b = 0; b < BB; ++b) {
-        const int tr = (wt * BB + b) * 16 + li;
+        const int tr = (wt + 4 * b) * 16 + li;
         if (tr >= nrows) continue;
         const int f = n0 + (wr * (AB / 2) + a) * 16 + 4 * lg;
         float v[4];
@@ -191,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     for (int a = 0; a < AB; ++a)
 #pragma unroll
       for (int b = 0; b < BB; ++b) {
-        const int tr = (wt * BB + b) * 16 + li;
+        const int tr = (wt + 4 * b) * 16 + li;
         if (tr >= nrows) continue;
         const int n = n0 + (wr * AB + a) * 16 + 4 * lg;
         store16(out + (int64_t)(r0 + tr) * N + n, u32x4_t{__float_as_uint(acc[a][b][0]), __float_as_uint(acc[a][b][1]),
