@@ -88,8 +88,10 @@ typedef struct {
                              1: y is fp32 and receives y += result (residual stream) */
   void* const* stage_events; /* optional instrumentation for moe_forward, or NULL: an array of
                                 2 * MOE_NUM_STAGES hipEvent_t (passed as void*, created by the
-                                caller); entry 2s is recorded on the stream just before stage s
-                                is launched and entry 2s+1 just after it. NULL entries are skipped. */
+                                caller); entries 2s and 2s+1 receive the start and the end of
+                                stage s's kernel, taken from the dispatch itself (no extra queue
+                                packets, so timing does not slow the step). NULL entries are
+                                skipped; with T = 0 nothing is launched or recorded. */
 } moe_opts;
 
 /* Stages of moe_forward, in launch order (one kernel each). */

@@ -7,6 +7,13 @@
 #include "launch.hpp"
 #include "moe.h"
 
+namespace moe {
+DispatchEvents& pending_dispatch_events() {
+  thread_local DispatchEvents ev;
+  return ev;
+}
+}  // namespace moe
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -256,36 +263,47 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   float* y_part = reinterpret_cast<float*>(ws + L.y_part);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  // Stage events: each stage is one kernel, which records its pair as its own dispatch
+  // timestamps (see launch_kernel); a pair the stage left unconsumed is recorded directly.
   void* const* ev = opts ? opts->stage_events : nullptr;
-  auto mark = [&](int i) -> moe_status {
-    if (!ev || !ev[i]) return MOE_OK;
-    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
-    return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  auto arm = [&](int st) {
+    if (ev) moe::pending_dispatch_events() = {static_cast<hipEvent_t>(ev[2 * st]), static_cast<hipEvent_t>(ev[2 * st + 1])};
+  };
+  auto disarm = [&]() -> moe_status {
+    moe::DispatchEvents& p = moe::pending_dispatch_events();
+    const moe::DispatchEvents left = p;
+    p = moe::DispatchEvents{};
+    for (hipEvent_t e : {left.start, left.stop}) {
+      if (!e) continue;
+      hipError_t r = hipEventRecord(e, s);
+      if (r != hipSuccess) return fail(MOE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(r));
+    }
+    return MOE_OK;
   };
 
-  MOE_TRY(mark(2 * MOE_STAGE_ROUTE));
+  arm(MOE_STAGE_ROUTE);
   moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
                     nullptr, s);
+  MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (route)"));
-  MOE_TRY(mark(2 * MOE_STAGE_ROUTE + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_PERMUTE));
+  arm(MOE_STAGE_PERMUTE);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
+  MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (permute)"));
-  MOE_TRY(mark(2 * MOE_STAGE_PERMUTE + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_UP));
+  arm(MOE_STAGE_EXPERT_UP);
   moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);
+  MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (expert up)"));
-  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_UP + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN));
+  arm(MOE_STAGE_EXPERT_DOWN);
   moe::launch_expert_down(m.dtype, m.weight_layout, h, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, L.ksplit, y_part,
                           s);
+  MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (expert down)"));
-  MOE_TRY(mark(2 * MOE_STAGE_EXPERT_DOWN + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
+  arm(MOE_STAGE_COMBINE);
   moe::launch_combine(y_perm, y_part, L.ksplit - 1, token_row, topk_w, m.T, m.d, m.K, yd, opts ? opts->accumulate : 0,
                       y, s);
-  MOE_TRY(check_launch("moe_forward (combine)"));
-  return mark(2 * MOE_STAGE_COMBINE + 1);
+  MOE_TRY(disarm());
+  return check_launch("moe_forward (combine)");
 }
 
 moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream) {

@@ -71,10 +71,10 @@ template <int MODE>
 void launch_mode(const float* y_perm, const float* y_part, int nparts, const int32_t* token_row, const float* topk_w,
                  int64_t T, int d, int K, void* y, hipStream_t stream) {
   if (T <= 1024) {
-    hipLaunchKernelGGL((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, y_part, nparts,
+    launch_kernel((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, y_part, nparts,
                        token_row, topk_w, T, d, K, y);
   } else {
-    hipLaunchKernelGGL((combine_kernel<MODE, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, y_perm, y_part,
+    launch_kernel((combine_kernel<MODE, 4>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, y_perm, y_part,
                        nparts, token_row, topk_w, T, d, K, y);
   }
 }
@@ -116,7 +116,7 @@ void launch_combine(const float* y_perm, const float* y_part, int nparts, const 
 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream) {
   const unsigned blocks = (unsigned)((T + 3) / 4);
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(blocks), dim3(256), 0, stream, h, T, d, eps, static_cast<bf16_t*>(x_bf16));
+  launch_kernel(rmsnorm_kernel, dim3(blocks), dim3(256), 0, stream, h, T, d, eps, static_cast<bf16_t*>(x_bf16));
 }
 
 }  // namespace moe

@@ -270,7 +270,7 @@ void launch_stream(const void* act, const int32_t* row_src, const int32_t* offse
   const int64_t max_tiles = (rows + TILE - 1) / TILE + E;
   const int64_t max_items = max_tiles * (N / (16 * RB));
   const int blocks = (int)std::min<int64_t>(max_items, resident_blocks(kernel, 256));
-  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, s, static_cast<const T*>(act), row_src, offsets,
+  launch_kernel(kernel, dim3(blocks), dim3(256), 0, s, static_cast<const T*>(act), row_src, offsets,
                      static_cast<const T*>(wa), static_cast<const T*>(wb), static_cast<OutT*>(out), K, N, E);
 }
 

@@ -1,10 +1,33 @@
 // Host-side launchers of the gfx950 kernels (internal to the library; the C ABI is in moe.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Dispatch timing. A caller arms a pair of events; the next kernel launched by the same host
+// thread records them as its own start and end timestamps (hipExtLaunchKernel), so timing adds
+// no packet to the queue (an hipEventRecord between two kernels holds the next dispatch back by
+// several microseconds). The launch disarms them.
+struct DispatchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+DispatchEvents& pending_dispatch_events();  // per host thread
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  DispatchEvents& ev = pending_dispatch_events();
+  if (ev.start || ev.stop) {
+    const DispatchEvents e = ev;
+    ev = DispatchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e.start, e.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;

@@ -32,10 +32,10 @@ void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_
   const int64_t pieces = (int64_t)E * N * K / V;
   const unsigned blocks = (unsigned)((pieces + 255) / 256);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(pack_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, static_cast<const bf16_t*>(w), pieces,
+    launch_kernel(pack_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, static_cast<const bf16_t*>(w), pieces,
                        N, K, static_cast<bf16_t*>(w_packed));
   else
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(w), pieces,
+    launch_kernel(pack_kernel<float>, dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(w), pieces,
                        N, K, static_cast<float*>(w_packed));
 }
 

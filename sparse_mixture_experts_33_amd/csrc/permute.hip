@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 template <int NT>
 void launch_index(const int32_t* idx, int64_t S, int K, int E, int32_t* counts, int32_t* offsets,
                   int32_t* row_token, int32_t* token_row, hipStream_t s) {
-  hipLaunchKernelGGL((permute_index_kernel<NT>), dim3(1), dim3(NT), (size_t)E * NT * sizeof(int32_t), s, idx, S, K,
+  launch_kernel((permute_index_kernel<NT>), dim3(1), dim3(NT), (size_t)E * NT * sizeof(int32_t), s, idx, S, K,
                      E, counts, offsets, row_token, token_row);
 }
 
@@ -112,7 +112,7 @@ void launch_permute_index(const int32_t* topk_idx, int64_t T, int E, int K, int3
 void launch_gather_rows(const void* x, const int32_t* row_token, int64_t rows, int64_t row_bytes, void* x_perm,
                         hipStream_t stream) {
   const unsigned blocks = (unsigned)((rows + 3) / 4);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint8_t*>(x),
+  launch_kernel(gather_rows_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint8_t*>(x),
                      row_token, rows, row_bytes, static_cast<uint8_t*>(x_perm));
 }
 

@@ -203,7 +203,7 @@ void launch(const void* x, const void* wg, const float* bias, int64_t T_, int d,
             float* w, float* logits, hipStream_t s) {
   const int64_t waves = (T_ + TPW - 1) / TPW;
   const unsigned blocks = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((route_kernel<T, EMAX, TPW>), dim3(blocks), dim3(256), 0, s, static_cast<const T*>(x),
+  launch_kernel((route_kernel<T, EMAX, TPW>), dim3(blocks), dim3(256), 0, s, static_cast<const T*>(x),
                      static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
 }
 
@@ -212,7 +212,7 @@ void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int 
               float* w, float* logits, hipStream_t s) {
   const bool many = T_ >= 4096;
   if (T_ <= 512 && E <= 8) {
-    hipLaunchKernelGGL((route_token_kernel<T, 8>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
+    launch_kernel((route_token_kernel<T, 8>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
                        static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
     return;
   }

@@ -245,7 +245,7 @@ void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
+  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                      static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
                      static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N);
 }

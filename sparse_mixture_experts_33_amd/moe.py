@@ -118,8 +118,9 @@ def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16, stage_
 def stage_event_array(events: dict):
     """ctypes array of 2*MOE_NUM_STAGES hipEvent_t handles for moe_opts.stage_events.
 
-    events maps an array position (2*stage for "before", 2*stage+1 for "after") to a raw
-    hipEvent_t handle (e.g. torch.cuda.Event(...).cuda_event); other positions stay NULL."""
+    events maps an array position (2*stage for the start, 2*stage+1 for the end of that stage's
+    kernel) to a raw hipEvent_t handle (e.g. torch.cuda.Event(...).cuda_event); other positions
+    stay NULL."""
     arr = (ctypes.c_void_p * (2 * MOE_NUM_STAGES))()
     for i, h in events.items():
         arr[i] = h
