@@ -51,6 +51,13 @@ def lib() -> ctypes.CDLL:
                                      vp, i32]
         L.oracle_rmsnorm_bf16.argtypes = [i64, i32, dbl, vp, vp, vp]
         L.oracle_deep_layer.argtypes = [i64, i32, i32, i32, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_forward_exact.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        L.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp]
+        L.oracle_backward_tokens.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                             i32]
+        L.oracle_backward_wsample.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp,
+                                              vp, i32]
         _lib = L
     return _lib
 
@@ -60,7 +67,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return 0
     if a.dtype == np.uint16:
         return 1
-    raise TypeError(f"storage dtype must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float64:
+        return 2
+    raise TypeError(f"storage dtype must be float32, uint16 (bf16 bits) or float64, got {a.dtype}")
 
 
 def _p(a):
@@ -174,3 +183,69 @@ def deep_layer(h, w_gate, w1, w3, w2, K, eps, bias=None, threads=0):
     lib().oracle_deep_layer(n, d, F, E, K, float(eps), _p(h), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2),
                             _p(idx), _p(logits), threads)
     return idx, logits
+
+
+# ----------------------------------------------------------------------------- backward pass
+# The pages define the forward layer only; the gradient follows from it by the chain rule with
+# the TopK selection held fixed (formulas in oracle.cpp). Gates come from the unrounded logits.
+
+def _layer_args(x, w_gate, w1, w3, w2, bias):
+    x, w_gate, w1, w3, w2 = _c(x), _c(w_gate), _c(w1), _c(w3), _c(w2)
+    dt = _dtype_code(x)
+    for a in (w_gate, w1, w3, w2):
+        assert _dtype_code(a) == dt
+    T, d = x.shape
+    E, F, _ = w1.shape
+    assert w_gate.shape == (d, E) and w3.shape == (E, F, d) and w2.shape == (E, d, F)
+    return x, w_gate, w1, w3, w2, _c(bias, np.float32), T, d, F, E, dt
+
+
+def forward_exact(x, w_gate, w1, w3, w2, K, bias=None, tokens=None):
+    """Forward with unrounded double logits (the function the backward differentiates).
+    Returns (y [n][d], idx [n][K])."""
+    x, w_gate, w1, w3, w2, bias, T, d, F, E, dt = _layer_args(x, w_gate, w1, w3, w2, bias)
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    n = tokens.shape[0]
+    y = np.empty((n, d), np.float64)
+    idx = np.empty((n, K), np.int32)
+    lib().oracle_forward_exact(d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n,
+                               _p(tokens), _p(y), _p(idx))
+    return y, idx
+
+
+def backward(x, w_gate, w1, w3, w2, K, dy, bias=None):
+    """Full backward (small shapes). Returns dict(dx, dlogits, dw_gate, dw1, dw3, dw2), float64."""
+    x, w_gate, w1, w3, w2, bias, T, d, F, E, dt = _layer_args(x, w_gate, w1, w3, w2, bias)
+    dy = _c(dy, np.float64)
+    assert dy.shape == (T, d)
+    out = {"dx": np.empty((T, d)), "dlogits": np.empty((T, E)), "dw_gate": np.empty((d, E)),
+           "dw1": np.empty((E, F, d)), "dw3": np.empty((E, F, d)), "dw2": np.empty((E, d, F))}
+    lib().oracle_backward(T, d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(dy),
+                          _p(out["dx"]), _p(out["dlogits"]), _p(out["dw_gate"]), _p(out["dw1"]), _p(out["dw3"]),
+                          _p(out["dw2"]))
+    return out
+
+
+def backward_tokens(x, w_gate, w1, w3, w2, K, dy, tokens, bias=None, threads=0):
+    """dx and dlogits of selected tokens: (dx [n][d], dlogits [n][E]), float64."""
+    x, w_gate, w1, w3, w2, bias, T, d, F, E, dt = _layer_args(x, w_gate, w1, w3, w2, bias)
+    dy = _c(dy, np.float64)
+    tokens = _c(tokens, np.int64)
+    n = tokens.shape[0]
+    dx = np.empty((n, d))
+    dl = np.empty((n, E))
+    lib().oracle_backward_tokens(d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(dy), n,
+                                 _p(tokens), _p(dx), _p(dl), threads)
+    return dx, dl
+
+
+def backward_wsample(x, w_gate, w1, w3, w2, K, dy, queries, bias=None, threads=0):
+    """Single weight-gradient entries. queries: int array [n][4] of (which, e, i, j) with which 1 (dw1[e][i][j]),
+    3 (dw3[e][i][j]) or 2 (dw2[e][i][j]). Returns float64 [n]."""
+    x, w_gate, w1, w3, w2, bias, T, d, F, E, dt = _layer_args(x, w_gate, w1, w3, w2, bias)
+    dy = _c(dy, np.float64)
+    q = _c(np.asarray(queries).reshape(-1, 4), np.int32)
+    val = np.empty(q.shape[0])
+    lib().oracle_backward_wsample(T, d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(dy),
+                                  q.shape[0], _p(q), _p(val), threads)
+    return val

@@ -31,8 +31,23 @@
  *   - the deep-stack layer is h <- h + MoE(bf16(h / sqrt(mean(h^2) + eps)))
  *     with a unit norm weight (the pages do not describe a norm).
  *
- * Storage types of inputs: dtype 0 = fp32, dtype 1 = bf16 bit patterns. A bf16
- * value is widened exactly (its 16 bits become the top half of an fp32).
+ * Storage types of inputs: dtype 0 = fp32, dtype 1 = bf16 bit patterns, dtype 2 =
+ * fp64 (used by the finite-difference checks of the backward pass). A bf16 value
+ * is widened exactly (its 16 bits become the top half of an fp32).
+ *
+ * Backward pass. The pages define only the forward layer; its gradient follows
+ * from that definition by the chain rule, with the TopK selection held fixed
+ * (it is piecewise constant in the inputs). For a token t with kept experts
+ * e_k, gates g_k and an upstream gradient dy_t:
+ *   o_k = w2[e_k] . h_k, h_k = silu(a_k) * b_k, a_k = w1[e_k] . x, b_k = w3[e_k] . x
+ *   dg_k = dy_t . o_k;  d logit_{e_k} = g_k (dg_k - sum_j g_j dg_j)   (softmax over the kept logits)
+ *   do_k = g_k dy_t;  dh_k = w2[e_k]^T do_k
+ *   da_k = dh_k * b_k * silu'(a_k),  db_k = dh_k * silu(a_k),  silu'(z) = s(z) (1 + z (1 - s(z)))
+ *   dx_t = sum_k (w1[e_k]^T da_k + w3[e_k]^T db_k) + W_g . d logit_t
+ *   dw2[e_k] += do_k h_k^T,  dw1[e_k] += da_k x^T,  dw3[e_k] += db_k x^T,  dW_g += x d logit_t^T
+ * The gates of the backward come from the unrounded double logits (the forward
+ * above uses fp32-rounded ones, a difference of ~1e-7 relative); the TopK
+ * decision is taken on fp32-rounded logits in both.
  */
 #include <cmath>
 #include <cstdint>
@@ -45,6 +60,7 @@ namespace {
 
 double load(const void* p, int dtype, int64_t i) {
   if (dtype == 0) return (double)static_cast<const float*>(p)[i];
+  if (dtype == 2) return static_cast<const double*>(p)[i];
   uint32_t bits = (uint32_t)static_cast<const uint16_t*>(p)[i] << 16;
   float f;
   std::memcpy(&f, &bits, 4);
@@ -85,20 +101,24 @@ void parallel_for(int64_t n, int threads, F body) {
   for (auto& t : pool) t.join();
 }
 
-// Router for one token: logits (fp32-rounded), TopK by repeated argmax, softmax of the kept ones.
+// Router for one token: logits, TopK by repeated argmax on the fp32-rounded logits, softmax of
+// the kept ones. round_logits: the returned logits (and so the gates) are the fp32-rounded values
+// (forward) or the unrounded double sums (backward and its finite-difference checks).
 void route_token(int d, int E, int K, int dtype, const void* x, int64_t t, const void* w_gate,
-                 const float* bias, double* logits, int32_t* idx, double* w) {
+                 const float* bias, double* logits, int32_t* idx, double* w, bool round_logits = true) {
+  std::vector<double> decide(E);
   for (int e = 0; e < E; ++e) {
     double s = 0.0;
     for (int k = 0; k < d; ++k) s += load(x, dtype, t * d + k) * load(w_gate, dtype, (int64_t)k * E + e);
     if (bias) s += (double)bias[e];
-    logits[e] = (double)(float)s;
+    decide[e] = (double)(float)s;
+    logits[e] = round_logits ? decide[e] : s;
   }
   std::vector<char> taken(E, 0);
   for (int j = 0; j < K; ++j) {
     int best = -1;
     for (int e = 0; e < E; ++e)
-      if (!taken[e] && (best < 0 || logits[e] > logits[best])) best = e;
+      if (!taken[e] && (best < 0 || decide[e] > decide[best])) best = e;
     taken[best] = 1;
     idx[j] = best;
   }
@@ -127,6 +147,91 @@ void expert_apply(int d, int F, int e, int dtype, const void* v, int64_t v_off, 
     double s = 0.0;
     for (int f = 0; f < F; ++f) s += load(w2, dtype, base2 + (int64_t)n * F + f) * hid[f];
     out[n] = s;
+  }
+}
+
+double dsilu(double z) {
+  const double s = 1.0 / (1.0 + std::exp(-z));
+  return s * (1.0 + z * (1.0 - s));
+}
+
+// Pieces of one kept (token, expert) pair that the backward needs, in double:
+// a = w1[e].x, b = w3[e].x (F-vectors) and, given the slot's output gradient do_k, dh = w2[e]^T do_k.
+void pair_hidden(int d, int F, int e, int dtype, const void* x, int64_t t, const void* w1, const void* w3,
+                 double* a, double* b) {
+  const int64_t base13 = (int64_t)e * F * d;
+  for (int f = 0; f < F; ++f) {
+    double sa = 0.0, sb = 0.0;
+    for (int k = 0; k < d; ++k) {
+      double xv = load(x, dtype, t * d + k);
+      sa += load(w1, dtype, base13 + (int64_t)f * d + k) * xv;
+      sb += load(w3, dtype, base13 + (int64_t)f * d + k) * xv;
+    }
+    a[f] = sa;
+    b[f] = sb;
+  }
+}
+
+// Backward of one token (formulas in the header). Adds its contributions to dx_t [d] and
+// dlog_t [E] (both zeroed here) and, when the pointers are non-null, to the weight gradients
+// dwg [d][E], dw1/dw3 [E][F][d], dw2 [E][d][F].
+void token_backward(int d, int F, int E, int K, int dtype, const void* x, int64_t t, const void* w_gate,
+                    const float* bias, const void* w1, const void* w3, const void* w2, const double* dy_t,
+                    double* dx_t, double* dlog_t, double* dwg, double* dw1, double* dw3, double* dw2) {
+  std::vector<double> logits(E), g(K), dg(K), a(F), b(F), h(F), dh(F), da(F), db(F), o(d);
+  std::vector<int32_t> idx(K);
+  route_token(d, E, K, dtype, x, t, w_gate, bias, logits.data(), idx.data(), g.data(), false);
+  for (int j = 0; j < d; ++j) dx_t[j] = 0.0;
+  for (int e = 0; e < E; ++e) dlog_t[e] = 0.0;
+  for (int k = 0; k < K; ++k) {
+    const int e = idx[k];
+    const int64_t base13 = (int64_t)e * F * d, base2 = (int64_t)e * d * F;
+    pair_hidden(d, F, e, dtype, x, t, w1, w3, a.data(), b.data());
+    for (int f = 0; f < F; ++f) h[f] = silu(a[f]) * b[f];
+    // o = w2[e] . h and dg_k = dy . o
+    double s_dg = 0.0;
+    for (int n = 0; n < d; ++n) {
+      double s = 0.0;
+      for (int f = 0; f < F; ++f) s += load(w2, dtype, base2 + (int64_t)n * F + f) * h[f];
+      o[n] = s;
+      s_dg += dy_t[n] * s;
+    }
+    dg[k] = s_dg;
+    // dh = w2[e]^T (g_k dy)
+    for (int f = 0; f < F; ++f) {
+      double s = 0.0;
+      for (int n = 0; n < d; ++n) s += load(w2, dtype, base2 + (int64_t)n * F + f) * g[k] * dy_t[n];
+      dh[f] = s;
+      da[f] = dh[f] * b[f] * dsilu(a[f]);
+      db[f] = dh[f] * silu(a[f]);
+    }
+    for (int j = 0; j < d; ++j) {
+      double s = 0.0;
+      for (int f = 0; f < F; ++f)
+        s += load(w1, dtype, base13 + (int64_t)f * d + j) * da[f] + load(w3, dtype, base13 + (int64_t)f * d + j) * db[f];
+      dx_t[j] += s;
+    }
+    if (dw2)
+      for (int n = 0; n < d; ++n)
+        for (int f = 0; f < F; ++f) dw2[base2 + (int64_t)n * F + f] += g[k] * dy_t[n] * h[f];
+    if (dw1)
+      for (int f = 0; f < F; ++f)
+        for (int j = 0; j < d; ++j) {
+          const double xv = load(x, dtype, t * d + j);
+          dw1[base13 + (int64_t)f * d + j] += da[f] * xv;
+          dw3[base13 + (int64_t)f * d + j] += db[f] * xv;
+        }
+  }
+  // softmax over the kept logits: d logit_{e_k} = g_k (dg_k - sum_j g_j dg_j)
+  double gdg = 0.0;
+  for (int k = 0; k < K; ++k) gdg += g[k] * dg[k];
+  for (int k = 0; k < K; ++k) dlog_t[idx[k]] = g[k] * (dg[k] - gdg);
+  for (int j = 0; j < d; ++j) {
+    double s = 0.0;
+    for (int e = 0; e < E; ++e) s += load(w_gate, dtype, (int64_t)j * E + e) * dlog_t[e];
+    dx_t[j] += s;
+    if (dwg)
+      for (int e = 0; e < E; ++e) dwg[(int64_t)j * E + e] += load(x, dtype, t * d + j) * dlog_t[e];
   }
 }
 
@@ -249,6 +354,87 @@ void oracle_deep_layer(int64_t n, int d, int F, int E, int K, double eps, double
   oracle_forward(n, d, F, E, K, 1, x.data(), w_gate, bias, w1, w3, w2, n, sel.data(), y.data(), logits_out,
                  idx_out, w.data(), threads);
   for (size_t i = 0; i < (size_t)n * d; ++i) h[i] += y[i];
+}
+
+// The forward above with unrounded double logits (gates from the exact logits, TopK decided on
+// fp32-rounded ones): the function whose gradient the backward computes. y_sel [n_sel][d].
+void oracle_forward_exact(int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
+                          const float* bias, const void* w1, const void* w3, const void* w2, int64_t n_sel,
+                          const int64_t* tok_sel, double* y_sel, int32_t* idx_sel) {
+  std::vector<double> logits(E), g(K), hid(F), o(d);
+  for (int64_t i = 0; i < n_sel; ++i) {
+    route_token(d, E, K, dtype, x, tok_sel[i], w_gate, bias, logits.data(), idx_sel + i * K, g.data(), false);
+    for (int n = 0; n < d; ++n) y_sel[i * d + n] = 0.0;
+    for (int k = 0; k < K; ++k) {
+      expert_apply(d, F, idx_sel[i * K + k], dtype, x, tok_sel[i] * d, dtype, w1, w3, w2, hid.data(), o.data());
+      for (int n = 0; n < d; ++n) y_sel[i * d + n] += g[k] * o[n];
+    }
+  }
+}
+
+// Full backward over all T tokens (small shapes): dy [T][d] -> dx [T][d], dlogits [T][E],
+// dwg [d][E], dw1, dw3 [E][F][d], dw2 [E][d][F]; all double, tokens accumulated in ascending order.
+void oracle_backward(int64_t T, int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
+                     const float* bias, const void* w1, const void* w3, const void* w2, const double* dy,
+                     double* dx, double* dlogits, double* dwg, double* dw1, double* dw3, double* dw2) {
+  std::fill(dwg, dwg + (int64_t)d * E, 0.0);
+  std::fill(dw1, dw1 + (int64_t)E * F * d, 0.0);
+  std::fill(dw3, dw3 + (int64_t)E * F * d, 0.0);
+  std::fill(dw2, dw2 + (int64_t)E * d * F, 0.0);
+  for (int64_t t = 0; t < T; ++t)
+    token_backward(d, F, E, K, dtype, x, t, w_gate, bias, w1, w3, w2, dy + t * d, dx + t * d, dlogits + t * E,
+                   dwg, dw1, dw3, dw2);
+}
+
+// Per-token part of the backward for selected tokens: dx_sel [n_sel][d], dlogits_sel [n_sel][E].
+void oracle_backward_tokens(int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
+                            const float* bias, const void* w1, const void* w3, const void* w2, const double* dy,
+                            int64_t n_sel, const int64_t* tok_sel, double* dx_sel, double* dlogits_sel, int threads) {
+  parallel_for(n_sel, threads, [&](int64_t i) {
+    const int64_t t = tok_sel[i];
+    token_backward(d, F, E, K, dtype, x, t, w_gate, bias, w1, w3, w2, dy + t * d, dx_sel + i * d,
+                   dlogits_sel + i * E, nullptr, nullptr, nullptr, nullptr);
+  });
+}
+
+// Single entries of the expert weight gradients, each summed over every (token, slot) routed to
+// its expert: query q = (which, e, i, j) with which 1: dw1[e][i][j], 3: dw3[e][i][j] (i < F, j < d),
+// 2: dw2[e][i][j] (i < d, j < F). val [n_q].
+void oracle_backward_wsample(int64_t T, int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
+                             const float* bias, const void* w1, const void* w3, const void* w2, const double* dy,
+                             int64_t n_q, const int32_t* q, double* val, int threads) {
+  std::vector<int32_t> idx((size_t)T * K);
+  std::vector<double> g((size_t)T * K), logits((size_t)T * E);
+  parallel_for(T, threads, [&](int64_t t) {
+    route_token(d, E, K, dtype, x, t, w_gate, bias, logits.data() + t * E, idx.data() + t * K, g.data() + t * K,
+                false);
+  });
+  parallel_for(n_q, threads, [&](int64_t u) {
+    const int which = q[4 * u], e = q[4 * u + 1], i = q[4 * u + 2], j = q[4 * u + 3];
+    const int64_t base13 = (int64_t)e * F * d, base2 = (int64_t)e * d * F;
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t)
+      for (int k = 0; k < K; ++k) {
+        if (idx[t * K + k] != e) continue;
+        const double gk = g[t * K + k];
+        const int f = which == 2 ? j : i;  // hidden unit of the entry
+        double a = 0.0, b = 0.0;
+        for (int m = 0; m < d; ++m) {
+          const double xv = load(x, dtype, t * d + m);
+          a += load(w1, dtype, base13 + (int64_t)f * d + m) * xv;
+          b += load(w3, dtype, base13 + (int64_t)f * d + m) * xv;
+        }
+        if (which == 2) {
+          acc += gk * dy[t * d + i] * silu(a) * b;  // do[i] * h[f]
+          continue;
+        }
+        double dh = 0.0;
+        for (int n = 0; n < d; ++n) dh += load(w2, dtype, base2 + (int64_t)n * F + f) * gk * dy[t * d + n];
+        const double xj = load(x, dtype, t * d + j);
+        acc += (which == 1 ? dh * b * dsilu(a) : dh * silu(a)) * xj;
+      }
+    val[u] = acc;
+  });
 }
 
 }  // extern "C"
