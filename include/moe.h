@@ -21,6 +21,7 @@
  *     moe_expert_ffn  grouped SwiGLU expert FFN over expert-contiguous rows
  *     moe_combine     gate-weighted sum back in token order
  *     moe_forward     all of the above in one call
+ * and moe_backward computes the gradients of the layer.
  *
  * Conventions shared by every call
  *  - Tensors are DEVICE pointers (hipMalloc'ed or torch CUDA/HIP tensors),
@@ -178,6 +179,34 @@ size_t moe_workspace_bytes(const moe_dims* dims);
 moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
                        const void* w3, const void* w2, void* y, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Backward pass of the layer (moe_forward with accumulate = 0). The pages define the forward
+ * only; its gradient follows by the chain rule with the TopK selection held fixed. For token t,
+ * kept experts e_k with gates g_k, a_k = w1[e_k] x, b_k = w3[e_k] x, h_k = silu(a_k) b_k,
+ * o_k = w2[e_k] h_k and upstream gradient dy:
+ *   dg_k = dy . o_k,  dlogit_{e_k} = g_k (dg_k - sum_j g_j dg_j)   (softmax over the kept logits)
+ *   dh_k = w2[e_k]^T (g_k dy),  da_k = dh_k * b_k * silu'(a_k),  db_k = dh_k * silu(a_k)
+ *   dx   = sum_k (w1[e_k]^T da_k + w3[e_k]^T db_k) + W_g dlogit
+ *   dw2[e] = sum (g_k dy) h_k^T,  dw1[e] = sum da_k x^T,  dw3[e] = sum db_k x^T,  dW_g = x^T dlogit
+ * The routing and a_k, b_k are recomputed from x (nothing is kept from the forward call).
+ *   x, w_gate, w1, w3, w2  as in moe_forward (dims->dtype = MOE_BF16, weights row-major)
+ *   dy       [T][d]    fp32 in   gradient of the loss with respect to y
+ *   dx       [T][d]    fp32 out
+ *   dw_gate  [d][E]    fp32 out
+ *   dw1, dw3 [E][F][d] fp32 out  (overwritten; an expert without tokens gets zeros)
+ *   dw2      [E][d][F] fp32 out
+ *   dlogits  [T][E]    fp32 out  optional (NULL = not written): gradient of the logits,
+ *                                zero for the experts not kept
+ *   workspace: >= moe_backward_workspace_bytes(dims) bytes of device memory, 256-byte aligned
+ * Operands of the matrix products are bf16 (dy, g_k dy, h_k, da_k and db_k rounded to nearest
+ * even); all sums are fp32 in a fixed order, so results are reproducible bit for bit.
+ * opts: gate_bias as in the forward; y_dtype, accumulate and stage_events are ignored.
+ * Supported: dims->dtype = MOE_BF16, weight_layout = MOE_LAYOUT_ROWMAJOR, d and F multiples of 256
+ * (with the general limits above); other valid arguments return MOE_ERR_UNSUPPORTED. */
+size_t moe_backward_workspace_bytes(const moe_dims* dims);
+moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
+                        const void* w3, const void* w2, const float* dy, float* dx, float* dw_gate, float* dw1,
+                        float* dw3, float* dw2, float* dlogits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm of a residual stream for a stack of mixture-of-experts layers (the pages
  * do not describe the norm; unit weight): x_bf16[t] = bf16(h[t] / sqrt(mean_j h[t][j]^2 + eps)),

@@ -26,7 +26,7 @@ _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libmoe_inputs.so")
 
 # tensor ids inside one layer
-X, W_GATE, W1, W3, W2, H0 = 0, 1, 2, 3, 4, 5
+X, W_GATE, W1, W3, W2, H0, DY = 0, 1, 2, 3, 4, 5, 6
 
 
 def build(force: bool = False) -> str:
@@ -162,6 +162,11 @@ def tokens(w: Workload) -> np.ndarray:
 def residual0(w: Workload) -> np.ndarray:
     """Initial residual stream h_0 [T][d] ~ N(0,1), fp32 (deep stack)."""
     return normal(key(w.seed, 0, H0), (w.T, w.d), 1.0, "f32")
+
+
+def upstream_grad(w: Workload) -> np.ndarray:
+    """dy [T][d] ~ N(0,1), fp32: the gradient of a loss with respect to the layer output (backward pass)."""
+    return normal(key(w.seed, 0, DY), (w.T, w.d), 1.0, "f32")
 
 
 def synthetic_routing(seed: int, T: int, E: int, K: int, skew: float = 0.0) -> np.ndarray:

@@ -7,6 +7,7 @@ SwiGLU experts (arXiv 2401.04088). ``moe`` is the ctypes binding of ``libmoe.so`
 from .moe import (  # noqa: F401
     MOE_BF16, MOE_F32, MOE_LAYOUT_PACKED, MOE_LAYOUT_ROWMAJOR, MOE_NUM_STAGES, MOE_STAGE_COMBINE,
     MOE_STAGE_EXPERT_DOWN, MOE_STAGE_EXPERT_UP, MOE_STAGE_PERMUTE, MOE_STAGE_ROUTE, MOE_W_DOWN, MOE_W_UP, Dims,
-    MoeError, lib, moe_abi_version, moe_combine, moe_expert_ffn, moe_forward, moe_last_error, moe_pack_weights,
-    moe_permute, moe_rmsnorm, moe_route, moe_status_string, moe_workspace_bytes, stage_event_array,
+    MoeError, lib, moe_abi_version, moe_backward, moe_backward_workspace_bytes, moe_combine, moe_expert_ffn,
+    moe_forward, moe_last_error, moe_pack_weights, moe_permute, moe_rmsnorm, moe_route, moe_status_string,
+    moe_workspace_bytes, stage_event_array,
 )

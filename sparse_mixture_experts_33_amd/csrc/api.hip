@@ -99,6 +99,61 @@ Workspace layout(const moe_dims& m) {
   return w;
 }
 
+// Backward workspace. ld: row stride of the transposed, group-padded activations (every group
+// padded to a multiple of 64 rows fits in roundup(T*K, 64) + 64*E columns).
+struct BwdWorkspace {
+  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, w2t, w13t, dy_perm, do_perm, dhp, h,
+      dab, dg, dlog, dxp, dwg_part, xT, dabT, doT, hT, total;
+  int64_t ld;
+};
+
+BwdWorkspace bwd_layout(const moe_dims& m) {
+  const size_t S = (size_t)m.T * m.K, d = (size_t)m.d, F = (size_t)m.F, E = (size_t)m.E;
+  BwdWorkspace w{};
+  w.ld = (int64_t)((S + 63) / 64 * 64 + 64 * E);
+  const size_t ld = (size_t)w.ld;
+  size_t o = 0;
+  auto take = [&](size_t& field, size_t bytes) {
+    field = o;
+    o = align256(o + bytes);
+  };
+  take(w.topk_idx, S * 4);
+  take(w.topk_w, S * 4);
+  take(w.counts, E * 4);
+  take(w.offsets, (E + 1) * 4);
+  take(w.row_token, S * 4);
+  take(w.token_row, S * 4);
+  take(w.x_perm, S * d * 2);
+  take(w.A, S * F * 4);
+  take(w.B, S * F * 4);
+  take(w.w2t, E * F * d * 2);
+  take(w.w13t, E * d * 2 * F * 2);
+  take(w.dy_perm, S * d * 2);
+  take(w.do_perm, S * d * 2);
+  take(w.dhp, S * F * 4);
+  take(w.h, S * F * 2);
+  take(w.dab, S * 2 * F * 2);
+  take(w.dg, S * 4);
+  take(w.dlog, (size_t)m.T * E * 4);
+  take(w.dxp, S * d * 4);
+  take(w.dwg_part, (size_t)moe::dwgate_chunks(m.T) * d * E * 4);
+  take(w.xT, d * ld * 2);
+  take(w.dabT, 2 * F * ld * 2);
+  take(w.doT, d * ld * 2);
+  take(w.hT, F * ld * 2);
+  w.total = o;
+  return w;
+}
+
+moe_status check_backward_sizes(const moe_dims& m) {
+  if (m.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass supports bf16 only (dtype = %d)", m.dtype);
+  if (m.weight_layout != MOE_LAYOUT_ROWMAJOR)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass takes row-major weights (weight_layout = %d)", m.weight_layout);
+  if (m.d % 256 != 0 || m.F % 256 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs d and F multiples of 256 (d = %d, F = %d)", m.d, m.F);
+  return MOE_OK;
+}
+
 const moe_opts kDefaultOpts = {nullptr, -1, 0, nullptr};
 
 moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
@@ -117,7 +172,7 @@ moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -304,6 +359,94 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
                       y, s);
   MOE_TRY(disarm());
   return check_launch("moe_forward (combine)");
+}
+
+size_t moe_backward_workspace_bytes(const moe_dims* dims) {
+  if (check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT) != MOE_OK) return 0;
+  if (check_backward_sizes(*dims) != MOE_OK) return 0;
+  return bwd_layout(*dims).total;
+}
+
+moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
+                        const void* w3, const void* w2, const float* dy, float* dx, float* dw_gate, float* dw1,
+                        float* dw3, float* dw2, float* dlogits, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT));
+  const moe_dims& m = *dims;
+  MOE_TRY(check_backward_sizes(m));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(dx, "dx"));
+  MOE_TRY(check_ptr(dw_gate, "dw_gate"));
+  MOE_TRY(check_ptr(dw1, "dw1"));
+  MOE_TRY(check_ptr(dw3, "dw3"));
+  MOE_TRY(check_ptr(dw2, "dw2"));
+  if (dlogits && !aligned16(dlogits)) return fail(MOE_ERR_INVALID_ARG, "dlogits is not 16-byte aligned");
+  int yd = 0;
+  MOE_TRY(check_opts(m, opts, &yd));
+  if (m.T == 0) return MOE_OK;
+  const BwdWorkspace L = bwd_layout(m);
+  MOE_TRY(check_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  int32_t* topk_idx = static_cast<int32_t*>(at(L.topk_idx));
+  float* topk_w = static_cast<float*>(at(L.topk_w));
+  int32_t* counts = static_cast<int32_t*>(at(L.counts));
+  int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
+  int32_t* row_token = static_cast<int32_t*>(at(L.row_token));
+  int32_t* token_row = static_cast<int32_t*>(at(L.token_row));
+  float* A = static_cast<float*>(at(L.A));
+  float* B = static_cast<float*>(at(L.B));
+  float* dhp = static_cast<float*>(at(L.dhp));
+  float* dg = static_cast<float*>(at(L.dg));
+  float* dlog = dlogits ? dlogits : static_cast<float*>(at(L.dlog));
+  float* dxp = static_cast<float*>(at(L.dxp));
+  char* dabT = static_cast<char*>(at(L.dabT));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t S = m.T * m.K;
+  const int rm = MOE_LAYOUT_ROWMAJOR;
+
+  // forward pieces: routing, permutation, gathered rows, pre-activations a = x.w1^T, b = x.w3^T
+  moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
+                    nullptr, s);
+  moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
+  moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
+  moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w1, A, 1, nullptr, s);
+  moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w3, B, 1, nullptr, s);
+  MOE_TRY(check_launch("moe_backward (recompute)"));
+  // transposed weights: w2t [E][F][d] = w2^T, w13t [E][d][2F] = [w1^T | w3^T]
+  moe::launch_transpose(w2, m.E, m.d, m.F, at(L.w2t), m.d, 0, s);
+  moe::launch_transpose(w1, m.E, m.F, m.d, at(L.w13t), 2 * (int64_t)m.F, 0, s);
+  moe::launch_transpose(w3, m.E, m.F, m.d, at(L.w13t), 2 * (int64_t)m.F, m.F, s);
+  // dh' = w2^T dy per row, then the SwiGLU and softmax derivatives
+  moe::launch_gather_dy(dy, row_token, token_row, topk_w, m.K, S, m.d, at(L.dy_perm), at(L.do_perm), s);
+  moe::launch_expert_down(m.dtype, rm, at(L.dy_perm), offsets, S, m.F, m.d, m.E, at(L.w2t), dhp, 1, nullptr, s);
+  moe::launch_swiglu_bwd(A, B, dhp, row_token, token_row, topk_w, m.K, S, m.F, at(L.h), at(L.dab), dg, s);
+  moe::launch_router_bwd(dg, token_row, topk_idx, topk_w, m.T, m.E, m.K, dlog, s);
+  MOE_TRY(check_launch("moe_backward (dgrad)"));
+  // dx = sum_k (w1^T da + w3^T db) + W_g dlogit; dW_g = x^T dlogit
+  moe::launch_expert_down(m.dtype, rm, at(L.dab), offsets, S, m.d, 2 * m.F, m.E, at(L.w13t), dxp, 1, nullptr, s);
+  moe::launch_dx(dxp, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
+  moe::launch_dwgate(x, dlog, m.T, m.d, m.E, static_cast<float*>(at(L.dwg_part)), dw_gate, s);
+  MOE_TRY(check_launch("moe_backward (dx)"));
+  // expert weight gradients: products over each group's rows of the transposed activations
+  moe::launch_group_transpose(at(L.x_perm), m.d, offsets, m.E, S, at(L.xT), L.ld, s);
+  moe::launch_group_transpose(at(L.dab), 2 * m.F, offsets, m.E, S, dabT, L.ld, s);
+  moe::launch_group_transpose(at(L.do_perm), m.d, offsets, m.E, S, at(L.doT), L.ld, s);
+  moe::launch_group_transpose(at(L.h), m.F, offsets, m.E, S, at(L.hT), L.ld, s);
+  moe::launch_tile_wgrad(dabT, m.F, at(L.xT), m.d, L.ld, offsets, m.E, dw1, s);
+  moe::launch_tile_wgrad(dabT + (size_t)m.F * L.ld * 2, m.F, at(L.xT), m.d, L.ld, offsets, m.E, dw3, s);
+  moe::launch_tile_wgrad(at(L.doT), m.d, at(L.hT), m.F, L.ld, offsets, m.E, dw2, s);
+  return check_launch("moe_backward (weight gradients)");
 }
 
 moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream) {

@@ -69,6 +69,13 @@ void launch_tile_up(int layout, const void* act, const int32_t* row_src, const i
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
+// Weight-gradient products of the backward pass (bf16 operands, fp32 out): for each expert e,
+// out[e][m][n] = sum over the rows r of e's group of pt[m][c_e + r] * qt[n][c_e + r]; pt [M][ld]
+// and qt [N][ld] hold the group-sorted rows transposed, group e from the padded column
+// c_e = sum_{e' < e} roundup(n_e', 64), zero beyond its rows. M, N multiples of 256, ld of 64.
+void launch_tile_wgrad(const void* pt, int M, const void* qt, int N, int64_t ld, const int32_t* offsets, int E,
+                       float* out, hipStream_t stream);
+
 // Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
 void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_packed, hipStream_t stream);
 
@@ -77,5 +84,27 @@ void launch_combine(const float* y_perm, const float* y_part, int nparts, const 
                     int64_t T, int d, int K, int y_dtype, int accumulate, void* y, hipStream_t stream);
 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream);
+
+// Backward pass (bf16 operands, fp32 sums; see backward.hip).
+// dst[b][c][col0 + r] = src[b][r][c] for src [B][R][C] bf16 (R, C multiples of 64), dst rows of stride ldd.
+void launch_transpose(const void* src, int B, int R, int C, void* dst, int64_t ldd, int col0, hipStream_t stream);
+// Group-sorted rows src [rows][M] bf16 -> dst [M][ld]: group e in columns c_e.. (zero padded to 64).
+void launch_group_transpose(const void* src, int M, const int32_t* offsets, int E, int64_t rows, void* dst, int64_t ld,
+                            hipStream_t stream);
+// dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]) for row r = (t, k) with gate g.
+void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
+                      int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t stream);
+// h = bf16(silu(A) B), dg = dh' . h, dab = [bf16(g dh' B silu'(A)) | bf16(g dh' silu(A))] per row.
+void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,
+                       const int32_t* token_row, const float* topk_w, int K, int64_t rows, int F, void* h, void* dab,
+                       float* dg, hipStream_t stream);
+void launch_router_bwd(const float* dg, const int32_t* token_row, const int32_t* topk_idx, const float* topk_w,
+                       int64_t T, int E, int K, float* dlogits, hipStream_t stream);
+void launch_dx(const float* dxp, const int32_t* token_row, const float* dlogits, const void* w_gate, int64_t T, int d,
+               int E, int K, float* dx, hipStream_t stream);
+// dW_g = x^T dlogits; part holds dwgate_chunks(T) * d * E floats.
+int dwgate_chunks(int64_t T);
+void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg,
+                   hipStream_t stream);
 
 }  // namespace moe

@@ -41,14 +41,21 @@ constexpr int kXcds = 8;
 
 __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 
-template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
+// WGRAD: weight-gradient mode of the backward pass. Per expert e the product runs over the rows of
+// e's group instead of over a fixed K: out[e][m][n] = sum_r act[m][c_e + r] * wa[n][c_e + r], where
+// act [M][K] and wa [N][K] hold the group-sorted rows transposed, each group starting at the padded
+// column c_e = sum_{e' < e} roundup(n_e', 64) (zero padding), and K is their row stride. The group
+// sizes come from `offsets` on the device. Tiles are (expert, n tile, m tile), one 256 x 256 output
+// tile each.
+template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, typename OutT>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
                                                            const int32_t* __restrict__ offsets,
                                                            const bf16_t* __restrict__ wa,
                                                            const bf16_t* __restrict__ wb, OutT* __restrict__ out,
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
-                                                           int64_t part_stride) {
+                                                           int64_t part_stride, int M) {
+  static_assert(!WGRAD || (!SWIGLU && !PACKED), "the weight-gradient mode is a plain product of row-major operands");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
   constexpr int TF = BT / 16 * 2;           // token fragments per k-step
@@ -73,8 +80,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   if (threadIdx.x == 0) {
     int acc = 0;
     for (int e = 0; e < E; ++e) {
-      s_tile0[e] = acc;
-      acc += (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
+      s_tile0[e] = acc;  // WGRAD: the group's padded first column; else its first tile
+      acc += WGRAD ? (s_off[e + 1] - s_off[e] + 63) / 64 * 64 : (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
     }
     s_tile0[E] = acc;
   }
@@ -82,20 +89,42 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   // Split-K (down projection only): every tile is computed as `ksplit` independent k-ranges;
   // range p > 0 writes its partial sums to part + (p-1)*part_stride, to be added in a fixed
   // order by the consumer.
-  const int total = s_tile0[E];
+  const int MT = WGRAD ? M / BT : 0;
+  const int total = WGRAD ? E * MT * NT : s_tile0[E];
   const int Q = (total * ksplit + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   if (j >= Q) return;
   const int tsplit = xcd * Q + j;
   if (tsplit >= total * ksplit) return;
   const int p = tsplit / total, tile = tsplit - p * total;
-  int e = 0;
-  while (tile >= s_tile0[e + 1]) ++e;
-  const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
-  const int local = tile - s_tile0[e];
-  const int nt = local / mtiles, mt = local - nt * mtiles;
-  const int r0 = __builtin_amdgcn_readfirstlane(s_off[e] + mt * BT);
-  const int nrows = __builtin_amdgcn_readfirstlane(min(BT, s_off[e + 1] - r0));
+  int e = 0, nt, mt, r0, nrows;
+  int64_t kcol0 = 0;  // first column of the tile's k range in both operands
+  int nsteps_all;
+  if constexpr (WGRAD) {
+    e = tile / (MT * NT);
+    const int local = tile - e * MT * NT;
+    nt = local / MT;
+    mt = local - nt * MT;
+    r0 = mt * BT;
+    nrows = min(BT, M - r0);
+    kcol0 = s_tile0[e];
+    nsteps_all = (s_off[e + 1] - s_off[e] + 63) / 64;
+    out += (int64_t)e * M * N;
+  } else {
+    while (tile >= s_tile0[e + 1]) ++e;
+    const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
+    const int local = tile - s_tile0[e];
+    nt = local / mtiles;
+    mt = local - nt * mtiles;
+    r0 = s_off[e] + mt * BT;
+    nrows = min(BT, s_off[e + 1] - r0);
+    nsteps_all = K / 64;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  kcol0 = __builtin_amdgcn_readfirstlane((int)kcol0);
+  nsteps_all = __builtin_amdgcn_readfirstlane(nsteps_all);
   // token blocks of this wavefront that hold at least one row of the group
   const int nbv = min(BB, max(0, ((nrows + 15) / 16 - wt + 3) / 4));
   const int n0 = nt * NW;
@@ -106,7 +135,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   // This wavefront loads fragments g = wave + 8*i of each stage: 16-row block (wave>>1) + 4*i at
   // the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
   const int qh = wave & 1, b0 = wave >> 1;
-  const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // first element row of the tile's weights
+  // first element of the tile's weights (WGRAD: the n rows of the shared operand at column kcol0)
+  const int64_t wrow0 = WGRAD ? (int64_t)n0 * K + kcol0 : ((int64_t)e * N + n0) * K;
   const int w_lane = PACKED ? qh * 512 + lane * 8 : (lane & 15) * K + qh * 32 + (lane >> 4) * 8;
   int32_t tsrc[TL];
 #pragma unroll
@@ -134,7 +164,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       wreg[i] = load16_nt(w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kWStep + w_lane);
     }
 #pragma unroll
-    for (int i = 0; i < TL; ++i) treg[i] = load16(act + (int64_t)tsrc[i] * K + (int64_t)s * 64 + t_lane);
+    for (int i = 0; i < TL; ++i) treg[i] = load16(act + (int64_t)tsrc[i] * K + kcol0 + (int64_t)s * 64 + t_lane);
   };
   auto lstore = [&](int stage) {
     uint8_t* base = smem + stage * STAGE;
@@ -189,7 +219,6 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     }
   };
 
-  const int nsteps_all = K / 64;
   const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
   auto kloop = [&](auto full) {
     gload(s_lo);
@@ -204,10 +233,12 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       __syncthreads();
     }
   };
-  if (nbv == BB)
-    kloop(std::true_type{});
-  else
-    kloop(std::false_type{});
+  if (s_lo < s_hi) {  // an empty group (WGRAD) leaves the accumulators at zero
+    if (nbv == BB)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+  }
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
   const int li = lane & 15, lg = lane >> 4;
@@ -245,9 +276,9 @@ void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
-                     static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
-                     static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N);
+  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
+                static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
+                static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0);
 }
 
 }  // namespace
@@ -278,6 +309,16 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
     }
   }
   return best;
+}
+
+void launch_tile_wgrad(const void* pt, int M, const void* qt, int N, int64_t ld, const int32_t* offsets, int E,
+                       float* out, hipStream_t s) {
+  const int64_t tiles = (int64_t)E * (M / 256) * (N / 256);
+  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, float>), dim3((unsigned)grid), dim3(512), 0, s,
+                static_cast<const bf16_t*>(pt), static_cast<const int32_t*>(nullptr), offsets,
+                static_cast<const bf16_t*>(qt), static_cast<const bf16_t*>(nullptr), out, (int)ld, N, E, 1,
+                static_cast<float*>(nullptr), (int64_t)0, M);
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,

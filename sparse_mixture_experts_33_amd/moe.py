@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 
 # every symbol include/moe.h declares
 SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_workspace_bytes",
-           "moe_forward", "moe_rmsnorm", "moe_status_string", "moe_last_error", "moe_abi_version")
+           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_rmsnorm", "moe_status_string",
+           "moe_last_error", "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -76,13 +77,17 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.argtypes = [P(moe_dims)]
         L.moe_workspace_bytes.restype = sz
         L.moe_forward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_backward_workspace_bytes.argtypes = [P(moe_dims)]
+        L.moe_backward_workspace_bytes.restype = sz
+        L.moe_backward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                   vp]
         L.moe_rmsnorm.argtypes = [i64, i32, f32, vp, vp, vp]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_forward",
-                     "moe_rmsnorm"):
+                     "moe_backward", "moe_rmsnorm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,6 +171,21 @@ def moe_forward(dims: Dims, x, w_gate, w1, w3, w2, y, workspace, gate_bias=None,
         workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
     _check(lib().moe_forward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
                              _ptr(w2), _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def moe_backward_workspace_bytes(dims: Dims) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def moe_backward(dims: Dims, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2, workspace, dlogits=None,
+                 gate_bias=None, stream=None, workspace_bytes=None):
+    """Gradients of the layer (include/moe.h, moe_backward). dy and every output are fp32 device tensors."""
+    o = _opts(gate_bias, dtype=dims.dtype)
+    nbytes = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
+    _check(lib().moe_backward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
+                              _ptr(w2), _ptr(dy), _ptr(dx), _ptr(dw_gate), _ptr(dw1), _ptr(dw3), _ptr(dw2),
+                              _ptr(dlogits), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def moe_rmsnorm(T: int, d: int, eps: float, h, x_bf16, stream=None):

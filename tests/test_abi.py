@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     assert [moe.moe_status_string(i) for i in range(5)] == list(moe.moe.STATUS.values())
 
 
@@ -112,3 +112,28 @@ def test_binding_raises_with_detail():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route(moe.Dims(4, 128, 256, 8, 9, 0), FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.status == 1 and "exceeds" in str(ei.value)
+
+
+def _backward(dims, ws=FAKE, nbytes=1 << 40, dy=FAKE, dlogits=None):
+    return moe.lib().moe_backward(ctypes.byref(dims), None, FAKE, FAKE, FAKE, FAKE, FAKE, dy, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, dlogits, ws, nbytes, None)
+
+
+def test_backward_validation():
+    L = moe.lib()
+    ok = moe_dims(64, 256, 512, 8, 2, 1, 0)
+    assert L.moe_backward_workspace_bytes(ctypes.byref(ok)) > 0
+    # supported sizes only: bf16, row-major weights, d and F multiples of 256
+    for bad in (moe_dims(64, 256, 512, 8, 2, 0, 0), moe_dims(64, 256, 512, 8, 2, 1, 1),
+                moe_dims(64, 192, 512, 8, 2, 1, 0), moe_dims(64, 256, 448, 8, 2, 1, 0)):
+        assert L.moe_backward_workspace_bytes(ctypes.byref(bad)) == 0
+        assert _backward(bad) == 2
+    assert _backward(moe_dims(64, 256, 512, 8, 9, 1, 0)) == 1       # K > E
+    assert _backward(ok, dy=None) == 1 and "dy" in moe.moe_last_error()
+    assert _backward(ok, dlogits=FAKE + 4) == 1                      # misaligned optional output
+    assert _backward(ok, nbytes=16) == 3                             # workspace too small
+    assert _backward(ok, ws=FAKE + 64) == 1                          # workspace not 256-byte aligned
+    assert _backward(moe_dims(0, 256, 512, 8, 2, 1, 0), ws=None, nbytes=0) == 0   # T = 0: nothing to do
+    # the workspace grows with the tokens
+    big = moe_dims(4096, 256, 512, 8, 2, 1, 0)
+    assert L.moe_backward_workspace_bytes(ctypes.byref(big)) > L.moe_backward_workspace_bytes(ctypes.byref(ok))
