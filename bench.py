@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--probe", choices=["copy"], help="plain copy of known size (counter calibration)")
+    p.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
+                   help="time moe_forward (default) or moe_backward (gradients of the layer)")
     return p.parse_args()
 
 
@@ -104,6 +106,9 @@ def main():
         return
 
     w = mi.WORKLOADS[args.workload]
+    if args.pass_ == "backward":
+        backward_bench(args, w)
+        return
     dt = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     s_x = 2 if w.dtype == "bf16" else 4
@@ -251,6 +256,102 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_host, host_layer0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+BWD_METRIC = "MoE-layer backward tokens/s + TFLOP/s vs peak (E=8,K=2,d=4096,F=14336)"
+
+
+def backward_bench(args, w):
+    """One step = one moe_backward call (routing and expert pre-activations recomputed from x; dx,
+    dW_g, dw1, dw3, dw2 in fp32) over the workload's tokens, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_33_amd as moe
+
+    assert w.dtype == "bf16" and w.layers == 1, "the backward pass is timed on one bf16 layer"
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    dims = moe.Dims(w.T, w.d, w.F, w.E, w.K, moe.MOE_BF16, moe.MOE_LAYOUT_ROWMAJOR)
+    W = mi.layer_weights(w)
+    L = {k: (dev(v) if v is not None else None) for k, v in W.items()}
+    x_host, dy_host = mi.tokens(w), mi.upstream_grad(w)
+    x, dy = dev(x_host), dev(dy_host)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty((w.T, w.d), **f32)
+    dwg = torch.empty((w.d, w.E), **f32)
+    dw1 = torch.empty((w.E, w.F, w.d), **f32)
+    dw3 = torch.empty((w.E, w.F, w.d), **f32)
+    dw2 = torch.empty((w.E, w.d, w.F), **f32)
+    ws = torch.empty(moe.moe_backward_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_backward(dims, x, L["w_gate"], L["w1"], L["w3"], L["w2"], dy, dx, dwg, dw1, dw3, dw2, ws,
+                         gate_bias=L["bias"])
+
+    for _ in range(args.warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic work of a backward pass: the gradient products w2^T dy, [w1|w3]^T [da|db] and the
+    # three weight gradients (6 T*K*d*F multiply-adds, twice the forward), plus the router's two
+    # T*d*E products. The recomputed forward products are implementation work, not counted.
+    S = w.T * w.K
+    flops = 12 * S * w.d * w.F + 4 * w.T * w.d * w.E
+    tf = flops / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": BWD_METRIC,
+        "value": round(w.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and upstream gradient, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "pass": "backward", "T": w.T, "d": w.d, "F": w.F, "E": w.E, "K": w.K,
+                   "weight_layout": "row-major", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_backward, whole call (HIP events around each call)", "kernel_ms": round(call_ms, 4),
+                     "algorithmic": {"flops": flops}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        sample = np.linspace(0, w.T - 1, 16).astype(np.int64)
+        done, reps, t1 = 0, 0, time.perf_counter()
+        while True:
+            oracle.backward_tokens(x_host, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, dy_host.astype(np.float64),
+                                   sample, bias=W["bias"], threads=threads)
+            done += len(sample)
+            reps += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"dx and logit gradients of {len(sample)} tokens x {reps} repetitions "
+                                         f"({el:.1f}s; the weight-gradient sums are not included)"}
     print(json.dumps(out), flush=True)
 
 

@@ -103,8 +103,9 @@ Workspace layout(const moe_dims& m) {
 // padded to a multiple of 64 rows fits in roundup(T*K, 64) + 64*E columns).
 struct BwdWorkspace {
   size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, w2t, w13t, dy_perm, do_perm, dhp, h,
-      dab, dg, dlog, dxp, dwg_part, xT, dabT, doT, hT, total;
+      dab, dg, dlog, dxp, dxp_part, dwg_part, xT, dabT, doT, hT, total;
   int64_t ld;
+  int dx_ksplit;  // k-ranges of the product [da|db] . [w1|w3] (partials 1.. at dxp_part)
 };
 
 BwdWorkspace bwd_layout(const moe_dims& m) {
@@ -136,6 +137,8 @@ BwdWorkspace bwd_layout(const moe_dims& m) {
   take(w.dg, S * 4);
   take(w.dlog, (size_t)m.T * E * 4);
   take(w.dxp, S * d * 4);
+  w.dx_ksplit = moe::tile_down_ksplit(m.dtype, (int64_t)S, m.E, m.d, 2 * m.F);
+  take(w.dxp_part, (size_t)(w.dx_ksplit - 1) * S * d * 4);
   take(w.dwg_part, (size_t)moe::dwgate_chunks(m.T) * d * E * 4);
   take(w.xT, d * ld * 2);
   take(w.dabT, 2 * F * ld * 2);
@@ -420,8 +423,12 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
                     nullptr, s);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
-  moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w1, A, 1, nullptr, s);
-  moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w3, B, 1, nullptr, s);
+  if (moe::tile_gemm_applies(m.dtype, S, m.E, m.d, m.F)) {
+    moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
+  } else {
+    moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w1, A, 1, nullptr, s);
+    moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w3, B, 1, nullptr, s);
+  }
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // transposed weights: w2t [E][F][d] = w2^T, w13t [E][d][2F] = [w1^T | w3^T]
   moe::launch_transpose(w2, m.E, m.d, m.F, at(L.w2t), m.d, 0, s);
@@ -434,8 +441,10 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   moe::launch_router_bwd(dg, token_row, topk_idx, topk_w, m.T, m.E, m.K, dlog, s);
   MOE_TRY(check_launch("moe_backward (dgrad)"));
   // dx = sum_k (w1^T da + w3^T db) + W_g dlogit; dW_g = x^T dlogit
-  moe::launch_expert_down(m.dtype, rm, at(L.dab), offsets, S, m.d, 2 * m.F, m.E, at(L.w13t), dxp, 1, nullptr, s);
-  moe::launch_dx(dxp, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
+  float* dxp_part = static_cast<float*>(at(L.dxp_part));
+  moe::launch_expert_down(m.dtype, rm, at(L.dab), offsets, S, m.d, 2 * m.F, m.E, at(L.w13t), dxp, L.dx_ksplit, dxp_part,
+                          s);
+  moe::launch_dx(dxp, dxp_part, L.dx_ksplit - 1, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
   moe::launch_dwgate(x, dlog, m.T, m.d, m.E, static_cast<float*>(at(L.dwg_part)), dw_gate, s);
   MOE_TRY(check_launch("moe_backward (dx)"));
   // expert weight gradients: products over each group's rows of the transposed activations

@@ -192,18 +192,27 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 }
 
 // dx[t] = sum_k dxp[token_row[t][k]] (slot order) + sum_e W_g[:, e] dlogit[t][e] (expert order).
+// When the product that wrote dxp was split into k-ranges, a row of dxp is first rebuilt as the
+// sum of its range partials in range order (part + p*part_stride, p < nparts).
 // One block per token, 4 columns per thread.
 template <int EMAX>
-__global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, const int32_t* __restrict__ token_row,
+__global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, const float* __restrict__ part,
+                                                 int nparts, int64_t part_stride, const int32_t* __restrict__ token_row,
                                                  const float* __restrict__ dlogits, const bf16_t* __restrict__ w_gate,
                                                  int d, int E, int K, float* __restrict__ dx) {
   const int64_t t = blockIdx.x;
   float dl[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) dl[e] = e < E ? dlogits[t * E + e] : 0.0f;
+  auto row = [&](int k, int c) {
+    const int64_t off = (int64_t)token_row[t * K + k] * d + c;
+    f32x4_t o = *reinterpret_cast<const f32x4_t*>(dxp + off);
+    for (int p = 0; p < nparts; ++p) o = o + *reinterpret_cast<const f32x4_t*>(part + p * part_stride + off);
+    return o;
+  };
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    f32x4_t s = *reinterpret_cast<const f32x4_t*>(dxp + (int64_t)token_row[t * K] * d + c);
-    for (int k = 1; k < K; ++k) s = s + *reinterpret_cast<const f32x4_t*>(dxp + (int64_t)token_row[t * K + k] * d + c);
+    f32x4_t s = row(0, c);
+    for (int k = 1; k < K; ++k) s = s + row(k, c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float rsum = 0.0f;
@@ -284,13 +293,16 @@ void launch_router_bwd(const float* dg, const int32_t* token_row, const int32_t*
                 T, E, K, dlogits);
 }
 
-void launch_dx(const float* dxp, const int32_t* token_row, const float* dlogits, const void* w_gate, int64_t T, int d,
-               int E, int K, float* dx, hipStream_t s) {
+void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* token_row, const float* dlogits,
+               const void* w_gate, int64_t T, int d, int E, int K, float* dx, hipStream_t s) {
   const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
+  const int64_t stride = T * K * (int64_t)d;
   if (E <= 8)
-    launch_kernel(dx_kernel<8>, dim3((unsigned)T), dim3(256), 0, s, dxp, token_row, dlogits, wg, d, E, K, dx);
+    launch_kernel(dx_kernel<8>, dim3((unsigned)T), dim3(256), 0, s, dxp, part, nparts, stride, token_row, dlogits, wg,
+                  d, E, K, dx);
   else
-    launch_kernel(dx_kernel<kMaxExperts>, dim3((unsigned)T), dim3(256), 0, s, dxp, token_row, dlogits, wg, d, E, K, dx);
+    launch_kernel(dx_kernel<kMaxExperts>, dim3((unsigned)T), dim3(256), 0, s, dxp, part, nparts, stride, token_row,
+                  dlogits, wg, d, E, K, dx);
 }
 
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg, hipStream_t s) {

@@ -66,6 +66,9 @@ bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F);
 int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F);
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+// Backward pass: the two pre-activations a = x.w1^T, b = x.w3^T (fp32) in one pass of the up tile.
+void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
+                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream);
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
@@ -100,8 +103,9 @@ void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const i
                        float* dg, hipStream_t stream);
 void launch_router_bwd(const float* dg, const int32_t* token_row, const int32_t* topk_idx, const float* topk_w,
                        int64_t T, int E, int K, float* dlogits, hipStream_t stream);
-void launch_dx(const float* dxp, const int32_t* token_row, const float* dlogits, const void* w_gate, int64_t T, int d,
-               int E, int K, float* dx, hipStream_t stream);
+// dxp rows are rebuilt from nparts extra k-range partials (part, each T*K*d) before the sum.
+void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* token_row, const float* dlogits,
+               const void* w_gate, int64_t T, int d, int E, int K, float* dx, hipStream_t stream);
 // dW_g = x^T dlogits; part holds dwgate_chunks(T) * d * E floats.
 int dwgate_chunks(int64_t T);
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg,

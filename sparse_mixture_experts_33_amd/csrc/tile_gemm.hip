@@ -242,7 +242,22 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
   const int li = lane & 15, lg = lane >> 4;
-  if constexpr (SWIGLU) {
+  if constexpr (SWIGLU && sizeof(OutT) == 4) {
+    // pre-activation pair (backward pass): a = x.w1^T to out, b = x.w3^T to part, both fp32
+#pragma unroll
+    for (int a = 0; a < AB / 2; ++a)
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        const int tr = (wt + 4 * b) * 16 + li;
+        if (tr >= nrows) continue;
+        const int64_t o = (int64_t)(r0 + tr) * N + n0 + (wr * (AB / 2) + a) * 16 + 4 * lg;
+        store16(out + o, u32x4_t{__float_as_uint(acc[a][b][0]), __float_as_uint(acc[a][b][1]),
+                                 __float_as_uint(acc[a][b][2]), __float_as_uint(acc[a][b][3])});
+        const f32x4_t& v = acc[a + AB / 2][b];
+        store16(part + o, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                  __float_as_uint(v[3])});
+      }
+  } else if constexpr (SWIGLU) {
 #pragma unroll
     for (int a = 0; a < AB / 2; ++a)
 #pragma unroll
@@ -327,6 +342,14 @@ void launch_tile_up(int layout, const void* act, const int32_t* row_src, const i
     launch_tile<256, 256, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
   else
     launch_tile<256, 256, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+}
+
+void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
+                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s) {
+  if (layout == kPacked)
+    launch_tile<256, 256, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
+  else
+    launch_tile<256, 256, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
