@@ -14,10 +14,10 @@
 // read of a wavefront is then one contiguous 1 KB, free of bank conflicts for any bank count.
 // Weights in the packed layout arrive already in that order (1 KB contiguous global loads).
 //
-// Tiles are numbered expert-major, then weight tile, then token tile, so the token tiles that
-// share one weight tile are adjacent; the linear index is remapped so that adjacent tiles go to
-// workgroups on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which keeps a
-// weight tile in that XCD's L2 while its token tiles run.
+// Tiles are numbered expert-major, then in bands of 4 token tiles, then weight tile, then token
+// tile within the band, so that the 32 tiles an XCD runs at once share 4 token and 8 weight row
+// blocks; the linear index is remapped so that adjacent tiles go to workgroups on the same XCD
+// (workgroups are dealt round-robin over the 8 XCDs), which keeps those blocks in that XCD's L2.
 //
 // Token blocks (16 rows) are dealt to the four token wavefronts round-robin (wavefront t owns
 // blocks t, t+4, t+8, t+12), so the partly filled last tile of a group spreads its rows over the
@@ -103,8 +103,18 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   if constexpr (WGRAD) {
     e = tile / (MT * NT);
     const int local = tile - e * MT * NT;
-    nt = local / MT;
-    mt = local - nt * MT;
+    // 32 consecutive tiles (the ones an XCD runs at once) form a 4 x 8 block of m x n tiles, so
+    // they share 4 + 8 operand row blocks instead of 32 + 1
+    constexpr int GM = 4, GN = 8;
+    if (MT % GM == 0 && NT % GN == 0) {
+      const int g = local / (GM * GN), w = local - g * (GM * GN);
+      const int gm = g % (MT / GM), gn = g / (MT / GM);
+      mt = gm * GM + w % GM;
+      nt = gn * GN + w / GM;
+    } else {
+      nt = local / MT;
+      mt = local - nt * MT;
+    }
     r0 = mt * BT;
     nrows = min(BT, M - r0);
     kcol0 = s_tile0[e];
@@ -114,8 +124,13 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     while (tile >= s_tile0[e + 1]) ++e;
     const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
     const int local = tile - s_tile0[e];
-    nt = local / mtiles;
-    mt = local - nt * mtiles;
+    // token tiles in bands of 4: within a band the token tile varies fastest, then the weight
+    // tile, so the 32 tiles an XCD runs at once cover 4 token x 8 weight tiles even for a group
+    // of many token tiles (a group of at most 4 is a single band: weight-tile major)
+    const int band = local / (4 * NT), mb = band * 4, bs = min(4, mtiles - mb);
+    const int w = local - band * 4 * NT;
+    mt = mb + w % bs;
+    nt = w / bs;
     r0 = s_off[e] + mt * BT;
     nrows = min(BT, s_off[e + 1] - r0);
     nsteps_all = K / 64;
