@@ -397,3 +397,57 @@ def test_forward_full_size_sampled(M, name):
     err = rel_err(y[tok][keep], r["y"][keep])
     say(f"  max|d|/max|ref| = {err:.3e} over {keep.sum()} sampled tokens")
     assert err <= tolerance(w.dtype)
+
+
+# ---------------------------------------------------------------- moe_forward against the stage calls
+
+FUSED = {
+    # small batches on the streaming kernels (moe_forward gathers the token rows inside the first
+    # GEMM; the stage calls gather them into x_perm first)
+    "fused_k2": mi.Workload("fused_k2", T=200, d=256, F=512, dtype="bf16", seed=631),
+    "fused_k1": mi.Workload("fused_k1", T=97, d=192, F=320, E=8, K=1, dtype="bf16", seed=632),
+    "fused_k4_e16": mi.Workload("fused_k4_e16", T=100, d=128, F=256, E=16, K=4, dtype="bf16", seed=633),
+    "fused_f32_k8": mi.Workload("fused_f32_k8", T=40, d=64, F=64, E=64, K=8, dtype="f32", seed=634),
+    "fused_decode": mi.Workload("fused_decode", T=32, d=4096, F=14336, dtype="bf16", seed=202),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+@pytest.mark.parametrize("mode", ["dtype", "f32", "accumulate"])
+def test_forward_bit_identical_to_stage_calls(M, name, mode):
+    """moe_forward against the four stage calls (route, permute with x_perm, expert FFN, combine) in
+    every output mode: the same arithmetic in the same order, so the outputs are bit-identical."""
+    w = FUSED[name]
+    say(f"[forward vs stages] {name} mode={mode}")
+    L = Layer(w)
+    dm = dims_of(M, w)
+    isbf = w.dtype == "bf16"
+    rng = np.random.default_rng(w.seed)
+    if mode == "accumulate":
+        y0 = rng.standard_normal((w.T, w.d)).astype(np.float32)
+        ya, yb = dev(y0), dev(y0)
+        yd = None
+    else:
+        tdt = torch.bfloat16 if (mode == "dtype" and isbf) else torch.float32
+        ya = torch.empty((w.T, w.d), dtype=tdt, device="cuda")
+        yb = torch.empty_like(ya)
+        yd = M.MOE_BF16 if tdt == torch.bfloat16 else M.MOE_F32
+    acc = mode == "accumulate"
+    ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+    M.moe_forward(dm, L.dx, L.dW["w_gate"], L.dW["w1"], L.dW["w3"], L.dW["w2"], ya, ws, gate_bias=L.dbias,
+                  y_dtype=yd, accumulate=acc)
+    S = w.T * w.K
+    i32 = dict(dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.T, w.K), **i32)
+    gw = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    counts, offsets = torch.empty(w.E, **i32), torch.empty(w.E + 1, **i32)
+    row_token, token_row = torch.empty(S, **i32), torch.empty((w.T, w.K), **i32)
+    x_perm = torch.empty((S, w.d), dtype=L.dx.dtype, device="cuda")
+    h = torch.empty((S, w.F), dtype=L.dx.dtype, device="cuda")
+    y_perm = torch.empty((S, w.d), dtype=torch.float32, device="cuda")
+    M.moe_route(dm, L.dx, L.dW["w_gate"], idx, gw, gate_bias=L.dbias)
+    M.moe_permute(dm, idx, L.dx, counts, offsets, row_token, token_row, x_perm)
+    M.moe_expert_ffn(dm, x_perm, offsets, L.dW["w1"], L.dW["w3"], L.dW["w2"], h, y_perm)
+    M.moe_combine(dm, y_perm, token_row, gw, yb, y_dtype=yd, accumulate=acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ya), host(yb))
