@@ -102,7 +102,7 @@ Workspace layout(const moe_dims& m) {
 // Backward workspace. ld: row stride of the transposed, group-padded activations (every group
 // padded to a multiple of 64 rows fits in roundup(T*K, 64) + 64*E columns).
 struct BwdWorkspace {
-  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, w2t, w13t, dy_perm, do_perm, dhp, h,
+  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, dy_perm, do_perm, dhp, h,
       dab, dg, dlog, dxp, dxp_part, dwg_part, xT, dabT, doT, hT, total;
   int64_t ld;
   int dx_ksplit;  // k-ranges of the product [da|db] . [w1|w3] (partials 1.. at dxp_part)
@@ -127,8 +127,6 @@ BwdWorkspace bwd_layout(const moe_dims& m) {
   take(w.x_perm, S * d * 2);
   take(w.A, S * F * 4);
   take(w.B, S * F * 4);
-  take(w.w2t, E * F * d * 2);
-  take(w.w13t, E * d * 2 * F * 2);
   take(w.dy_perm, S * d * 2);
   take(w.do_perm, S * d * 2);
   take(w.dhp, S * F * 4);
@@ -418,32 +416,25 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   const int64_t S = m.T * m.K;
   const int rm = MOE_LAYOUT_ROWMAJOR;
 
+  // Every product below runs on the LDS-tiled kernels (any group size is handled; token blocks past
+  // a group's end cost no MFMAs); the ones on transposed weights read w2 and w1, w3 as they lie.
   // forward pieces: routing, permutation, gathered rows, pre-activations a = x.w1^T, b = x.w3^T
   moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
                     nullptr, s);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
-  if (moe::tile_gemm_applies(m.dtype, S, m.E, m.d, m.F)) {
-    moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
-  } else {
-    moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w1, A, 1, nullptr, s);
-    moe::launch_expert_down(m.dtype, rm, at(L.x_perm), offsets, S, m.F, m.d, m.E, w3, B, 1, nullptr, s);
-  }
+  moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
   MOE_TRY(check_launch("moe_backward (recompute)"));
-  // transposed weights: w2t [E][F][d] = w2^T, w13t [E][d][2F] = [w1^T | w3^T]
-  moe::launch_transpose(w2, m.E, m.d, m.F, at(L.w2t), m.d, 0, s);
-  moe::launch_transpose(w1, m.E, m.F, m.d, at(L.w13t), 2 * (int64_t)m.F, 0, s);
-  moe::launch_transpose(w3, m.E, m.F, m.d, at(L.w13t), 2 * (int64_t)m.F, m.F, s);
-  // dh' = w2^T dy per row, then the SwiGLU and softmax derivatives
+  // dh' = w2^T dy per row (w2 [E][d][F] is the transposed weight of this product), then the SwiGLU
+  // and softmax derivatives
   moe::launch_gather_dy(dy, row_token, token_row, topk_w, m.K, S, m.d, at(L.dy_perm), at(L.do_perm), s);
-  moe::launch_expert_down(m.dtype, rm, at(L.dy_perm), offsets, S, m.F, m.d, m.E, at(L.w2t), dhp, 1, nullptr, s);
+  moe::launch_tile_wt(at(L.dy_perm), offsets, S, m.F, m.d, m.E, w2, nullptr, dhp, 1, nullptr, s);
   moe::launch_swiglu_bwd(A, B, dhp, row_token, token_row, topk_w, m.K, S, m.F, at(L.h), at(L.dab), dg, s);
   moe::launch_router_bwd(dg, token_row, topk_idx, topk_w, m.T, m.E, m.K, dlog, s);
   MOE_TRY(check_launch("moe_backward (dgrad)"));
   // dx = sum_k (w1^T da + w3^T db) + W_g dlogit; dW_g = x^T dlogit
   float* dxp_part = static_cast<float*>(at(L.dxp_part));
-  moe::launch_expert_down(m.dtype, rm, at(L.dab), offsets, S, m.d, 2 * m.F, m.E, at(L.w13t), dxp, L.dx_ksplit, dxp_part,
-                          s);
+  moe::launch_tile_wt(at(L.dab), offsets, S, m.d, 2 * m.F, m.E, w1, w3, dxp, L.dx_ksplit, dxp_part, s);
   moe::launch_dx(dxp, dxp_part, L.dx_ksplit - 1, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
   moe::launch_dwgate(x, dlog, m.T, m.d, m.E, static_cast<float*>(at(L.dwg_part)), dw_gate, s);
   MOE_TRY(check_launch("moe_backward (dx)"));

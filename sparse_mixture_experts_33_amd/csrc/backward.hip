@@ -3,7 +3,7 @@
 // over the kept logits, y = sum_k g_k E_k(x) with SwiGLU experts: blog.csdn.net explainer,
 // sections 1 and 2.1-2.4; xyznot.com summary, "Método"); its gradient follows by the chain rule
 // with the TopK selection held fixed. For a row r = (token t, slot k) of expert e, gate g_k:
-//   dh'_r = w2[e]^T dy_t                        (grouped GEMM on W2 transposed)
+//   dh'_r = w2[e]^T dy_t                        (grouped GEMM reading w2 as its transposed weight)
 //   dg_k  = dh'_r . h_r                         (= dy_t . o_r, since o_r = w2[e] h_r)
 //   dh_r  = g_k dh'_r,  da_r = dh_r * b_r * silu'(a_r),  db_r = dh_r * silu(a_r)
 //   dlogit_{e_k} = g_k (dg_k - sum_j g_j dg_j)  (softmax over the kept logits)
@@ -32,34 +32,6 @@ __device__ inline float row_gate(const int32_t* row_token, const int32_t* token_
     if (token_row[(int64_t)t * K + k] == r) g = topk_w[(int64_t)t * K + k];
   t_out = t;
   return g;
-}
-
-// dst[b][c][col0 + r] = src[b][r][c]: src [B][R][C], dst rows of stride ldd, B batches of C rows.
-// 64 x 64 tiles through LDS (rows padded by one element against bank conflicts).
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ src, int R, int C,
-                                                        bf16_t* __restrict__ dst, int64_t ldd, int col0) {
-  __shared__ bf16_t tile[64][64 + 2];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  const bf16_t* s = src + b * R * C;
-  bf16_t* o = dst + b * C * ldd;
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int rr = i / 8, cc = (i % 8) * 8;
-    const u32x4_t v = load16(s + (int64_t)(r0 + rr) * C + c0 + cc);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[rr][cc + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
-      tile[rr][cc + 2 * q + 1] = (bf16_t)(v[q] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int cc = i / 8, rr = (i % 8) * 8;
-    u32x4_t v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[rr + 2 * q][cc] | ((uint32_t)tile[rr + 2 * q + 1][cc] << 16);
-    store16(o + (int64_t)(c0 + cc) * ldd + col0 + r0 + rr, v);
-  }
 }
 
 // Group-sorted rows [rows][M] -> transposed [M][ld]: the rows of expert e land in columns
@@ -261,11 +233,6 @@ __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict
 }  // namespace
 
 int dwgate_chunks(int64_t T) { return (int)((T + kDwgChunk - 1) / kDwgChunk); }
-
-void launch_transpose(const void* src, int B, int R, int C, void* dst, int64_t ldd, int col0, hipStream_t s) {
-  launch_kernel(transpose_kernel, dim3((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)B), dim3(256), 0, s,
-                static_cast<const bf16_t*>(src), R, C, static_cast<bf16_t*>(dst), ldd, col0);
-}
 
 void launch_group_transpose(const void* src, int M, const int32_t* offsets, int E, int64_t rows, void* dst, int64_t ld,
                             hipStream_t s) {

@@ -66,6 +66,12 @@ bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F);
 int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F);
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+// Grouped product with transposed weights (backward pass): out[r][n] = sum_k act[r][k] W_e[k][n] for the
+// rows r of group e, W_e [K][N] row-major; wa holds k < K/2 and wb the rest when wb is given (wb
+// NULL: wa holds all K). fp32 out, split into ksplit k-ranges as launch_tile_down. N multiple of 256,
+// K of 64 (of 128 with wb).
+void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
+                    const void* wb, float* out, int ksplit, float* part, hipStream_t stream);
 // Backward pass: the two pre-activations a = x.w1^T, b = x.w3^T (fp32) in one pass of the up tile.
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream);
@@ -89,8 +95,6 @@ void launch_combine(const float* y_perm, const float* y_part, int nparts, const 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream);
 
 // Backward pass (bf16 operands, fp32 sums; see backward.hip).
-// dst[b][c][col0 + r] = src[b][r][c] for src [B][R][C] bf16 (R, C multiples of 64), dst rows of stride ldd.
-void launch_transpose(const void* src, int B, int R, int C, void* dst, int64_t ldd, int col0, hipStream_t stream);
 // Group-sorted rows src [rows][M] bf16 -> dst [M][ld]: group e in columns c_e.. (zero padded to 64).
 void launch_group_transpose(const void* src, int M, const int32_t* offsets, int E, int64_t rows, void* dst, int64_t ld,
                             hipStream_t stream);

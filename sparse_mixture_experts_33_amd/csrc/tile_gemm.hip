@@ -47,7 +47,15 @@ __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 // column c_e = sum_{e' < e} roundup(n_e', 64) (zero padding), and K is their row stride. The group
 // sizes come from `offsets` on the device. Tiles are (expert, n tile, m tile), one 256 x 256 output
 // tile each.
-template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, typename OutT>
+//
+// WT: the weight operand is stored transposed, [E][K][N] with the N columns contiguous (the layout
+// in which the backward pass holds w2 and w1, w3 for its products): wa holds k < KA = K/2 and wb
+// the rest when wb is given (KA = K otherwise). A k-step of the weight block is staged in LDS as
+// it lies in memory (64 rows of 256 columns, rows padded by 16 elements), and each matrix-core
+// operand is assembled by two transposing LDS reads (ds_read_b64_tr_b16): in each group of 16
+// lanes, lanes 4a..4a+3 address the 16 columns of row a, and lane i receives column i of the 4
+// rows, which is 4 consecutive k of weight row i.
+template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
                                                            const int32_t* __restrict__ offsets,
@@ -56,6 +64,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
                                                            int64_t part_stride, int M) {
   static_assert(!WGRAD || (!SWIGLU && !PACKED), "the weight-gradient mode is a plain product of row-major operands");
+  static_assert(!WT || (!SWIGLU && !PACKED && !WGRAD), "transposed weights: plain product only");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
   constexpr int TF = BT / 16 * 2;           // token fragments per k-step
@@ -64,7 +73,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   constexpr int TL = TF / NWV;              // token fragment loads per wavefront per step
   constexpr int AB = BW / 32;               // weight blocks per wavefront
   constexpr int BB = BT / 64;               // token blocks per wavefront
-  constexpr int STAGE = (WF + TF) * 1024;   // bytes per LDS stage
+  constexpr int WROW = BW + 16;             // WT: LDS row of the weight block (elements, padded)
+  constexpr int WPART = WT ? 64 * WROW * 2 : WF * 1024;  // bytes of the weight block per stage
+  constexpr int STAGE = WPART + TF * 1024;  // bytes per LDS stage
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ int32_t s_off[kMaxExperts + 1];
@@ -164,8 +175,19 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   // k advance per step: packed weights move 2 fragments (1024 elements) per 16-row block
   constexpr int64_t kWStep = PACKED ? 1024 : 64;
 
+  // WT: thread loads 8 consecutive columns nc.. of k rows kr0 + 16*i of the step (coalesced rows)
+  const int kr0 = threadIdx.x / (BW / 8), nc = (threadIdx.x % (BW / 8)) * 8;
+  const int KA = (WT && wb) ? K / 2 : K;
   u32x4_t wreg[WL], treg[TL];
   auto gload = [&](int s) {
+    if constexpr (WT) {
+      const bool second = wb && s * 64 >= KA;  // uniform over the step (KA is a multiple of 64)
+      const bf16_t* w = second ? wb : wa;
+      const int64_t k0 = (int64_t)s * 64 - (second ? KA : 0);
+#pragma unroll
+      for (int i = 0; i < WL; ++i)
+        wreg[i] = load16_nt(w + ((int64_t)e * KA + k0 + kr0 + (512 / (BW / 8)) * i) * N + n0 + nc);
+    } else
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
       int blk = b0 + 4 * i;
@@ -184,9 +206,29 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   auto lstore = [&](int stage) {
     uint8_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < WL; ++i) store16(base + (wave + 8 * i) * 1024 + lane * 16, wreg[i]);
+    for (int i = 0; i < WL; ++i) {
+      if constexpr (WT)
+        store16(base + ((kr0 + (512 / (BW / 8)) * i) * WROW + nc) * 2, wreg[i]);
+      else
+        store16(base + (wave + 8 * i) * 1024 + lane * 16, wreg[i]);
+    }
 #pragma unroll
-    for (int i = 0; i < TL; ++i) store16(base + WF * 1024 + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
+    for (int i = 0; i < TL; ++i) store16(base + WPART + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
+  };
+  // Weight operand of 16-row block blk at k-half q (16 rows x 32 k, lane l: row l%16, k 8(l/16)..+7).
+  auto wfrag = [&](const uint8_t* base, int blk, int q) -> u32x4_t {
+    if constexpr (WT) {
+      typedef __attribute__((ext_vector_type(4))) short v4s;
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const int g = lane >> 4, a = (lane >> 2) & 3, c = lane & 3;
+      const uint8_t* p = base + ((q * 32 + 8 * g + a) * WROW + blk * 16 + 4 * c) * 2;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * WROW * 2));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    } else {
+      return load16(base + (blk * 2 + q) * 1024 + lane * 16);
+    }
   };
 
   f32x4_t acc[AB][BB];
@@ -203,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
   // Token fragment of the wavefront's b-th token block (block wt + 4b) at k-half q.
   auto tfrag = [&](const uint8_t* base, int b, int q) {
-    return load16(base + WF * 1024 + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
+    return load16(base + WPART + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
   };
   // Multiply one LDS stage. FULL: all BB token blocks of the wavefront hold rows; otherwise only
   // the first nbv do (the last, partly filled tile of a group).
@@ -212,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     for (int q = 0; q < 2; ++q) {
       u32x4_t A[AB];
 #pragma unroll
-      for (int a = 0; a < AB; ++a) A[a] = load16(base + (wblock(a) * 2 + q) * 1024 + lane * 16);
+      for (int a = 0; a < AB; ++a) A[a] = wfrag(base, wblock(a), q);
       if constexpr (decltype(full)::value) {
         u32x4_t B[BB];
 #pragma unroll
@@ -300,13 +342,13 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   }
 }
 
-template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT>
+template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false>
 void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
                  const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
+  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
                 static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0);
 }
@@ -345,7 +387,7 @@ void launch_tile_wgrad(const void* pt, int M, const void* qt, int N, int64_t ld,
                        float* out, hipStream_t s) {
   const int64_t tiles = (int64_t)E * (M / 256) * (N / 256);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, float>), dim3((unsigned)grid), dim3(512), 0, s,
+  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, false, float>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(pt), static_cast<const int32_t*>(nullptr), offsets,
                 static_cast<const bf16_t*>(qt), static_cast<const bf16_t*>(nullptr), out, (int)ld, N, E, 1,
                 static_cast<float*>(nullptr), (int64_t)0, M);
@@ -365,6 +407,11 @@ void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, co
     launch_tile<256, 256, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
   else
     launch_tile<256, 256, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
+}
+
+void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
+                    const void* wb, float* out, int ksplit, float* part, hipStream_t s) {
+  launch_tile<256, 256, false, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part, s);
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
