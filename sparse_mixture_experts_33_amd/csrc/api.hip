@@ -99,20 +99,16 @@ Workspace layout(const moe_dims& m) {
   return w;
 }
 
-// Backward workspace. ld: row stride of the transposed, group-padded activations (every group
-// padded to a multiple of 64 rows fits in roundup(T*K, 64) + 64*E columns).
+// Backward workspace.
 struct BwdWorkspace {
   size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, dy_perm, do_perm, dhp, h,
-      dab, dg, dlog, dxp, dxp_part, dwg_part, xT, dabT, doT, hT, total;
-  int64_t ld;
+      dab, dg, dlog, dxp, dxp_part, dwg_part, total;
   int dx_ksplit;  // k-ranges of the product [da|db] . [w1|w3] (partials 1.. at dxp_part)
 };
 
 BwdWorkspace bwd_layout(const moe_dims& m) {
   const size_t S = (size_t)m.T * m.K, d = (size_t)m.d, F = (size_t)m.F, E = (size_t)m.E;
   BwdWorkspace w{};
-  w.ld = (int64_t)((S + 63) / 64 * 64 + 64 * E);
-  const size_t ld = (size_t)w.ld;
   size_t o = 0;
   auto take = [&](size_t& field, size_t bytes) {
     field = o;
@@ -138,10 +134,6 @@ BwdWorkspace bwd_layout(const moe_dims& m) {
   w.dx_ksplit = moe::tile_down_ksplit(m.dtype, (int64_t)S, m.E, m.d, 2 * m.F);
   take(w.dxp_part, (size_t)(w.dx_ksplit - 1) * S * d * 4);
   take(w.dwg_part, (size_t)moe::dwgate_chunks(m.T) * d * E * 4);
-  take(w.xT, d * ld * 2);
-  take(w.dabT, 2 * F * ld * 2);
-  take(w.doT, d * ld * 2);
-  take(w.hT, F * ld * 2);
   w.total = o;
   return w;
 }
@@ -411,7 +403,6 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   float* dg = static_cast<float*>(at(L.dg));
   float* dlog = dlogits ? dlogits : static_cast<float*>(at(L.dlog));
   float* dxp = static_cast<float*>(at(L.dxp));
-  char* dabT = static_cast<char*>(at(L.dabT));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t S = m.T * m.K;
   const int rm = MOE_LAYOUT_ROWMAJOR;
@@ -438,14 +429,11 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   moe::launch_dx(dxp, dxp_part, L.dx_ksplit - 1, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
   moe::launch_dwgate(x, dlog, m.T, m.d, m.E, static_cast<float*>(at(L.dwg_part)), dw_gate, s);
   MOE_TRY(check_launch("moe_backward (dx)"));
-  // expert weight gradients: products over each group's rows of the transposed activations
-  moe::launch_group_transpose(at(L.x_perm), m.d, offsets, m.E, S, at(L.xT), L.ld, s);
-  moe::launch_group_transpose(at(L.dab), 2 * m.F, offsets, m.E, S, dabT, L.ld, s);
-  moe::launch_group_transpose(at(L.do_perm), m.d, offsets, m.E, S, at(L.doT), L.ld, s);
-  moe::launch_group_transpose(at(L.h), m.F, offsets, m.E, S, at(L.hT), L.ld, s);
-  moe::launch_tile_wgrad(dabT, m.F, at(L.xT), m.d, L.ld, offsets, m.E, dw1, s);
-  moe::launch_tile_wgrad(dabT + (size_t)m.F * L.ld * 2, m.F, at(L.xT), m.d, L.ld, offsets, m.E, dw3, s);
-  moe::launch_tile_wgrad(at(L.doT), m.d, at(L.hT), m.F, L.ld, offsets, m.E, dw2, s);
+  // expert weight gradients: products over each group's rows, read as they lie
+  const uint16_t* dab = static_cast<const uint16_t*>(at(L.dab));  // bf16 [T*K][2F]
+  moe::launch_tile_wgrad(dab, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw1, s);
+  moe::launch_tile_wgrad(dab + m.F, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw3, s);
+  moe::launch_tile_wgrad(at(L.do_perm), m.d, m.d, at(L.h), m.F, m.F, offsets, m.E, dw2, s);
   return check_launch("moe_backward (weight gradients)");
 }
 

@@ -34,56 +34,6 @@ __device__ inline float row_gate(const int32_t* row_token, const int32_t* token_
   return g;
 }
 
-// Group-sorted rows [rows][M] -> transposed [M][ld]: the rows of expert e land in columns
-// c_e .. c_e + n_e - 1, c_e = sum_{e' < e} roundup(n_e', 64); columns up to c_e + roundup(n_e, 64)
-// are zero. One block per (64 columns of M, 64 output columns); since every c_e is a multiple of
-// 64, an output tile belongs to one group.
-__global__ __launch_bounds__(256) void group_transpose_kernel(const bf16_t* __restrict__ src, int M,
-                                                              const int32_t* __restrict__ offsets, int E,
-                                                              bf16_t* __restrict__ dst, int64_t ld) {
-  __shared__ bf16_t tile[64][64 + 2];
-  __shared__ int s_g[2];  // first source row of the tile, rows of the tile that exist
-  const int m0 = blockIdx.x * 64;
-  const int64_t c0 = (int64_t)blockIdx.y * 64;
-  if (threadIdx.x == 0) {
-    int64_t c = 0;
-    int first = 0, valid = -1;
-    for (int e = 0; e < E; ++e) {
-      const int n = offsets[e + 1] - offsets[e];
-      const int64_t pad = (n + 63) / 64 * 64;
-      if (c0 < c + pad) {
-        first = offsets[e] + (int)(c0 - c);
-        valid = min(64, offsets[e + 1] - first);
-        break;
-      }
-      c += pad;
-    }
-    s_g[0] = first;
-    s_g[1] = valid;
-  }
-  __syncthreads();
-  const int first = s_g[0], valid = s_g[1];
-  if (valid < 0) return;  // past the last group: columns never read
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int rr = i / 8, cc = (i % 8) * 8;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (rr < valid) v = load16(src + (int64_t)(first + rr) * M + m0 + cc);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[rr][cc + 2 * q] = (bf16_t)(v[q] & 0xFFFFu);
-      tile[rr][cc + 2 * q + 1] = (bf16_t)(v[q] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int mm = i / 8, rr = (i % 8) * 8;
-    u32x4_t v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[rr + 2 * q][mm] | ((uint32_t)tile[rr + 2 * q + 1][mm] << 16);
-    store16(dst + (int64_t)(m0 + mm) * ld + c0 + rr, v);
-  }
-}
-
 // Per row r = (t, k): dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g_k dy[t]). One block per row.
 __global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict__ dy, const int32_t* __restrict__ row_token,
                                                         const int32_t* __restrict__ token_row,
@@ -233,13 +183,6 @@ __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict
 }  // namespace
 
 int dwgate_chunks(int64_t T) { return (int)((T + kDwgChunk - 1) / kDwgChunk); }
-
-void launch_group_transpose(const void* src, int M, const int32_t* offsets, int E, int64_t rows, void* dst, int64_t ld,
-                            hipStream_t s) {
-  (void)rows;
-  launch_kernel(group_transpose_kernel, dim3((unsigned)(M / 64), (unsigned)(ld / 64)), dim3(256), 0, s,
-                static_cast<const bf16_t*>(src), M, offsets, E, static_cast<bf16_t*>(dst), ld);
-}
 
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t s) {

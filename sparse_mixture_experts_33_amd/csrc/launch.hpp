@@ -79,10 +79,9 @@ void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
 // Weight-gradient products of the backward pass (bf16 operands, fp32 out): for each expert e,
-// out[e][m][n] = sum over the rows r of e's group of pt[m][c_e + r] * qt[n][c_e + r]; pt [M][ld]
-// and qt [N][ld] hold the group-sorted rows transposed, group e from the padded column
-// c_e = sum_{e' < e} roundup(n_e', 64), zero beyond its rows. M, N multiples of 256, ld of 64.
-void launch_tile_wgrad(const void* pt, int M, const void* qt, int N, int64_t ld, const int32_t* offsets, int E,
+// out[e][m][n] = sum over the rows r of e's group of p[r][m] * q[r][n], p and q group-sorted rows of
+// strides ldp and ldq. M and N multiples of 256.
+void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int ldq, const int32_t* offsets, int E,
                        float* out, hipStream_t stream);
 
 // Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
@@ -95,9 +94,6 @@ void launch_combine(const float* y_perm, const float* y_part, int nparts, const 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream);
 
 // Backward pass (bf16 operands, fp32 sums; see backward.hip).
-// Group-sorted rows src [rows][M] bf16 -> dst [M][ld]: group e in columns c_e.. (zero padded to 64).
-void launch_group_transpose(const void* src, int M, const int32_t* offsets, int E, int64_t rows, void* dst, int64_t ld,
-                            hipStream_t stream);
 // dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]) for row r = (t, k) with gate g.
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t stream);

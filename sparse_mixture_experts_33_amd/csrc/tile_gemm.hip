@@ -42,11 +42,12 @@ constexpr int kXcds = 8;
 __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 
 // WGRAD: weight-gradient mode of the backward pass. Per expert e the product runs over the rows of
-// e's group instead of over a fixed K: out[e][m][n] = sum_r act[m][c_e + r] * wa[n][c_e + r], where
-// act [M][K] and wa [N][K] hold the group-sorted rows transposed, each group starting at the padded
-// column c_e = sum_{e' < e} roundup(n_e', 64) (zero padding), and K is their row stride. The group
-// sizes come from `offsets` on the device. Tiles are (expert, n tile, m tile), one 256 x 256 output
-// tile each.
+// e's group instead of over a fixed K: out[e][m][n] = sum over the group's rows r of
+// act[r][m] * wa[r][n], with act [rows][.] (row stride K) and wa [rows][.] (row stride ldw) the
+// group-sorted rows as they lie (WGRAD requires WT: both operands k-major, read through transposing
+// LDS reads). A k-step takes 64 rows of the group; rows past its end are zeroed in registers. The
+// group sizes come from `offsets` on the device. Tiles are (expert, n tile, m tile), one 256 x 256
+// output tile each.
 //
 // WT: the weight operand is stored transposed, [E][K][N] with the N columns contiguous (the layout
 // in which the backward pass holds w2 and w1, w3 for its products): wa holds k < KA = K/2 and wb
@@ -62,9 +63,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ wa,
                                                            const bf16_t* __restrict__ wb, OutT* __restrict__ out,
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
-                                                           int64_t part_stride, int M) {
-  static_assert(!WGRAD || (!SWIGLU && !PACKED), "the weight-gradient mode is a plain product of row-major operands");
-  static_assert(!WT || (!SWIGLU && !PACKED && !WGRAD), "transposed weights: plain product only");
+                                                           int64_t part_stride, int M, int ldw) {
+  static_assert(!WGRAD || (!SWIGLU && !PACKED && WT), "the weight-gradient mode reads both operands k-major");
+  static_assert(!WT || (!SWIGLU && !PACKED), "transposed weights: plain product only");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
   constexpr int TF = BT / 16 * 2;           // token fragments per k-step
@@ -75,7 +76,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   constexpr int BB = BT / 64;               // token blocks per wavefront
   constexpr int WROW = BW + 16;             // WT: LDS row of the weight block (elements, padded)
   constexpr int WPART = WT ? 64 * WROW * 2 : WF * 1024;  // bytes of the weight block per stage
-  constexpr int STAGE = WPART + TF * 1024;  // bytes per LDS stage
+  constexpr int TROW = BT + 16;             // WGRAD: LDS row of the token block (elements, padded)
+  constexpr int TPART = WGRAD ? 64 * TROW * 2 : TF * 1024;
+  constexpr int STAGE = WPART + TPART;      // bytes per LDS stage
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ int32_t s_off[kMaxExperts + 1];
@@ -91,8 +94,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   if (threadIdx.x == 0) {
     int acc = 0;
     for (int e = 0; e < E; ++e) {
-      s_tile0[e] = acc;  // WGRAD: the group's padded first column; else its first tile
-      acc += WGRAD ? (s_off[e + 1] - s_off[e] + 63) / 64 * 64 : (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
+      s_tile0[e] = acc;  // first tile of the group
+      acc += WGRAD ? 0 : (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
     }
     s_tile0[E] = acc;
   }
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     }
     r0 = mt * BT;
     nrows = min(BT, M - r0);
-    kcol0 = s_tile0[e];
+    kcol0 = s_off[e];  // first row of the group: the k range starts there
     nsteps_all = (s_off[e + 1] - s_off[e] + 63) / 64;
     out += (int64_t)e * M * N;
   } else {
@@ -161,8 +164,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   // This wavefront loads fragments g = wave + 8*i of each stage: 16-row block (wave>>1) + 4*i at
   // the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
   const int qh = wave & 1, b0 = wave >> 1;
-  // first element of the tile's weights (WGRAD: the n rows of the shared operand at column kcol0)
-  const int64_t wrow0 = WGRAD ? (int64_t)n0 * K + kcol0 : ((int64_t)e * N + n0) * K;
+  // first element of the tile's weights (row-major and packed layouts)
+  const int64_t wrow0 = ((int64_t)e * N + n0) * K;
   const int w_lane = PACKED ? qh * 512 + lane * 8 : (lane & 15) * K + qh * 32 + (lane >> 4) * 8;
   int32_t tsrc[TL];
 #pragma unroll
@@ -179,14 +182,29 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   const int kr0 = threadIdx.x / (BW / 8), nc = (threadIdx.x % (BW / 8)) * 8;
   const int KA = (WT && wb) ? K / 2 : K;
   u32x4_t wreg[WL], treg[TL];
+  const int kend = WGRAD ? s_off[e + 1] : 0, klast = WGRAD ? s_off[E] - 1 : 0;  // group end, last row
   auto gload = [&](int s) {
+    if constexpr (WGRAD) {
+      // both operands: rows kcol0 + 64 s + kr of the group, zero past its end (loads clamped in bounds)
+#pragma unroll
+      for (int i = 0; i < WL; ++i) {
+        const int kr = (int)kcol0 + s * 64 + kr0 + (512 / (BW / 8)) * i;
+        const int64_t kc = min(kr, klast);
+        const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t wv = load16_nt(wa + kc * ldw + n0 + nc);
+        const u32x4_t tv = load16(act + kc * K + r0 + nc);
+        wreg[i] = kr < kend ? wv : z;
+        treg[i] = kr < kend ? tv : z;
+      }
+      return;
+    }
     if constexpr (WT) {
       const bool second = wb && s * 64 >= KA;  // uniform over the step (KA is a multiple of 64)
       const bf16_t* w = second ? wb : wa;
       const int64_t k0 = (int64_t)s * 64 - (second ? KA : 0);
 #pragma unroll
       for (int i = 0; i < WL; ++i)
-        wreg[i] = load16_nt(w + ((int64_t)e * KA + k0 + kr0 + (512 / (BW / 8)) * i) * N + n0 + nc);
+        wreg[i] = load16_nt(w + ((int64_t)e * KA + k0 + kr0 + (512 / (BW / 8)) * i) * ldw + n0 + nc);
     } else
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
@@ -213,22 +231,31 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         store16(base + (wave + 8 * i) * 1024 + lane * 16, wreg[i]);
     }
 #pragma unroll
-    for (int i = 0; i < TL; ++i) store16(base + WPART + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
+    for (int i = 0; i < TL; ++i) {
+      if constexpr (WGRAD)
+        store16(base + WPART + ((kr0 + (512 / (BT / 8)) * i) * TROW + nc) * 2, treg[i]);
+      else
+        store16(base + WPART + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
+    }
+  };
+  // Matrix-core operand from a k-major block in LDS (64 rows of `row` elements): 16 columns
+  // blk*16.. at k-half q, lane l gets column l%16 at k = 8(l/16)..+7 (two transposing reads).
+  auto trfrag = [&](const uint8_t* blkbase, int row, int blk, int q) -> u32x4_t {
+    typedef __attribute__((ext_vector_type(4))) short v4s;
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const int g = lane >> 4, a = (lane >> 2) & 3, c = lane & 3;
+    const uint8_t* p = blkbase + ((q * 32 + 8 * g + a) * row + blk * 16 + 4 * c) * 2;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * row * 2));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
   };
   // Weight operand of 16-row block blk at k-half q (16 rows x 32 k, lane l: row l%16, k 8(l/16)..+7).
   auto wfrag = [&](const uint8_t* base, int blk, int q) -> u32x4_t {
-    if constexpr (WT) {
-      typedef __attribute__((ext_vector_type(4))) short v4s;
-      typedef __attribute__((address_space(3))) v4s* lds_v4s;
-      const int g = lane >> 4, a = (lane >> 2) & 3, c = lane & 3;
-      const uint8_t* p = base + ((q * 32 + 8 * g + a) * WROW + blk * 16 + 4 * c) * 2;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * WROW * 2));
-      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-    } else {
+    if constexpr (WT)
+      return trfrag(base, WROW, blk, q);
+    else
       return load16(base + (blk * 2 + q) * 1024 + lane * 16);
-    }
   };
 
   f32x4_t acc[AB][BB];
@@ -244,8 +271,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   };
 
   // Token fragment of the wavefront's b-th token block (block wt + 4b) at k-half q.
-  auto tfrag = [&](const uint8_t* base, int b, int q) {
-    return load16(base + WPART + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
+  auto tfrag = [&](const uint8_t* base, int b, int q) -> u32x4_t {
+    if constexpr (WGRAD)
+      return trfrag(base + WPART, TROW, wt + 4 * b, q);
+    else
+      return load16(base + WPART + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
   };
   // Multiply one LDS stage. FULL: all BB token blocks of the wavefront hold rows; otherwise only
   // the first nbv do (the last, partly filled tile of a group).
@@ -350,7 +380,7 @@ void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
   launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
-                static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0);
+                static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0, N);
 }
 
 }  // namespace
@@ -383,14 +413,14 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   return best;
 }
 
-void launch_tile_wgrad(const void* pt, int M, const void* qt, int N, int64_t ld, const int32_t* offsets, int E,
+void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int ldq, const int32_t* offsets, int E,
                        float* out, hipStream_t s) {
   const int64_t tiles = (int64_t)E * (M / 256) * (N / 256);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, false, float>), dim3((unsigned)grid), dim3(512), 0, s,
-                static_cast<const bf16_t*>(pt), static_cast<const int32_t*>(nullptr), offsets,
-                static_cast<const bf16_t*>(qt), static_cast<const bf16_t*>(nullptr), out, (int)ld, N, E, 1,
-                static_cast<float*>(nullptr), (int64_t)0, M);
+  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, true, float>), dim3((unsigned)grid), dim3(512), 0, s,
+                static_cast<const bf16_t*>(p), static_cast<const int32_t*>(nullptr), offsets,
+                static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(nullptr), out, ldp, N, E, 1,
+                static_cast<float*>(nullptr), (int64_t)0, M, ldq);
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
