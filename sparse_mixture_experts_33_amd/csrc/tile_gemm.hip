@@ -5,7 +5,7 @@
 //   C[w][t] = sum_k W[w][k] * X[t][k]     (w: weight row = output column, t: token row of the group)
 //
 // Workgroup tile: BW weight rows x BT tokens (SwiGLU: BW/2 rows of w1 and the same BW/2 rows of
-// w3, so that silu(a)*b is formed in registers), k-steps of 64, two LDS stages. Eight wavefronts
+// w3, so that silu(a)*b is formed in registers), 128 KB of LDS stages. Eight wavefronts
 // (two per SIMD, so one's LDS and memory waits overlap the other's MFMAs) in a 2 x 4
 // arrangement, each BW/2 weight rows x BT/4 tokens, 16x16x32 bf16 MFMAs accumulating in fp32.
 //
@@ -24,9 +24,20 @@
 // SIMDs; a wavefront skips the MFMAs (and fragment reads) of blocks that lie wholly past the
 // group's end. Token rows past the end still load a valid row and are never stored.
 //
-// k loop, per step s: write step s+1 (loaded into registers during step s-1) to the free LDS
-// stage, load step s+2 into registers, multiply step s out of LDS, barrier. Writing at the start
-// of the step, not just before the barrier, lets the LDS writes complete under the MFMAs instead
+// Forward products (weights [E][N][K], packed or row-major): k-steps of 32 through four LDS stages
+// of 32 KB, filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// the destination + 16 l, which is fragment order), so three steps are in flight while one is
+// multiplied and no registers stage the data. Per step s: wait until this wavefront's loads of
+// step s have landed (vmcnt, counting the loads issued after them), barrier (then every
+// wavefront's have), issue step s+3 into the stage that step s-1 used, read the fragments of step
+// s, multiply. The fragment reads are inline assembly that waits for its own results: the
+// compiler cannot tell them apart from the asynchronous LDS writes and would otherwise wait for
+// every load in flight before each read; for the same reason the barrier is a bare s_barrier
+// (a workgroup fence makes the compiler drain all loads first).
+//
+// Backward products (WT, WGRAD): k-steps of 64 through two stages staged in registers. Per step s:
+// write step s+1 (loaded during step s-1) to the free stage, load step s+2, multiply step s,
+// barrier. Writing at the start of the step lets the LDS writes complete under the MFMAs instead
 // of holding every wavefront at the barrier.
 #include "common.hpp"
 #include "launch.hpp"
@@ -307,24 +318,144 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   };
 
   const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
-  auto kloop = [&](auto full) {
-    gload(s_lo);
-    lstore(0);
-    if (s_lo + 1 < s_hi) gload(s_lo + 1);
-    __syncthreads();
-    for (int s = s_lo; s < s_hi; ++s) {
-      const int cur = (s - s_lo) & 1;
-      if (s + 1 < s_hi) lstore(cur ^ 1);
-      if (s + 2 < s_hi) gload(s + 2);
-      if (decltype(full)::value || nbv > 0) compute(smem + cur * STAGE, full);
-      __syncthreads();
+  if constexpr (!WT && !WGRAD) {
+    // forward: k-steps of 32, four stages of 32 KB (16 weight then 16 token fragments), direct loads
+    constexpr int SB = 32768;
+    static_assert(BW == 256 && BT == 256, "stage layout below assumes 256 x 256 tiles");
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int s0 = s_lo * 2, s1 = s_hi * 2;
+    int32_t trow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (wave + 8 * i) * 16 + (lane & 15);
+      const int r = r0 + (rr < nrows ? rr : 0);
+      trow[i] = row_src ? row_src[r] : r;
     }
-  };
-  if (s_lo < s_hi) {  // an empty group (WGRAD) leaves the accumulators at zero
-    if (nbv == BB)
-      kloop(std::true_type{});
-    else
-      kloop(std::false_type{});
+    const int wl32 = PACKED ? lane * 8 : (lane & 15) * K + (lane >> 4) * 8;
+    constexpr int64_t kW32 = PACKED ? 512 : 32;
+    auto dma = [&](int s) {
+      uint8_t* base = smem + (s & 3) * SB;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int blk = wave + 8 * i;
+        const bf16_t* w = wa;
+        if constexpr (SWIGLU) {
+          if (i == 1) {
+            w = wb;
+            blk -= 8;
+          }
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kW32 + wl32),
+                                         (lds_ptr)(base + (wave + 8 * i) * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
+            (lds_ptr)(base + 16384 + (wave + 8 * i) * 1024), 16, 0, 0);
+    };
+    // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
+    // fragment (block wt); the others are at the constant offsets in the reads below
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+    const uint32_t aoff = lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
+    const uint32_t boff = lds0 + 16384 + wt * 1024 + lane * 16;
+    auto run = [&](auto full) {
+      for (int i = 0; i < 3; ++i)
+        if (s0 + i < s1) dma(s0 + i);
+      for (int s = s0; s < s1; ++s) {
+        const int ahead = min(2, s1 - 1 - s);  // steps issued after s (4 loads each)
+        if (ahead >= 2)
+          __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt(8)
+        else if (ahead == 1)
+          __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4)
+        else
+          __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        // a bare barrier: a fence here would make the compiler wait for every load in flight
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 3 < s1) dma(s + 3);
+        const uint32_t st = (uint32_t)(s & 3) * SB;
+        const uint32_t av = aoff + st, bv = boff + st;
+        // weight blocks wblock(0..7) (SwiGLU: 4 of w1, then the same 4 of w3, 8 blocks apart) and
+        // token blocks wt + 4b; early-clobber outputs, since the reads are in flight together
+        u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3;
+        if constexpr (SWIGLU) {
+          asm volatile(
+              "ds_read_b128 %0, %12 offset:0\n"
+              "ds_read_b128 %1, %12 offset:1024\n"
+              "ds_read_b128 %2, %12 offset:2048\n"
+              "ds_read_b128 %3, %12 offset:3072\n"
+              "ds_read_b128 %4, %12 offset:8192\n"
+              "ds_read_b128 %5, %12 offset:9216\n"
+              "ds_read_b128 %6, %12 offset:10240\n"
+              "ds_read_b128 %7, %12 offset:11264\n"
+              "ds_read_b128 %8, %13 offset:0\n"
+              "ds_read_b128 %9, %13 offset:4096\n"
+              "ds_read_b128 %10, %13 offset:8192\n"
+              "ds_read_b128 %11, %13 offset:12288\n"
+              "s_waitcnt lgkmcnt(0)\n"
+              : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
+                "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
+              : "v"(av), "v"(bv)
+              : "memory");
+        } else {
+          asm volatile(
+              "ds_read_b128 %0, %12 offset:0\n"
+              "ds_read_b128 %1, %12 offset:1024\n"
+              "ds_read_b128 %2, %12 offset:2048\n"
+              "ds_read_b128 %3, %12 offset:3072\n"
+              "ds_read_b128 %4, %12 offset:4096\n"
+              "ds_read_b128 %5, %12 offset:5120\n"
+              "ds_read_b128 %6, %12 offset:6144\n"
+              "ds_read_b128 %7, %12 offset:7168\n"
+              "ds_read_b128 %8, %13 offset:0\n"
+              "ds_read_b128 %9, %13 offset:4096\n"
+              "ds_read_b128 %10, %13 offset:8192\n"
+              "ds_read_b128 %11, %13 offset:12288\n"
+              "s_waitcnt lgkmcnt(0)\n"
+              : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
+                "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
+              : "v"(av), "v"(bv)
+              : "memory");
+        }
+        const u32x4_t A[8] = {A0, A1, A2, A3, A4, A5, A6, A7};
+        const u32x4_t B[4] = {B0, B1, B2, B3};
+#pragma unroll
+        for (int b = 0; b < BB; ++b) {
+          if (decltype(full)::value || b < nbv) {
+#pragma unroll
+            for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+          }
+        }
+      }
+    };
+    if (s0 < s1) {
+      if (nbv == BB)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+    }
+  } else {
+    auto kloop = [&](auto full) {
+      gload(s_lo);
+      lstore(0);
+      if (s_lo + 1 < s_hi) gload(s_lo + 1);
+      __syncthreads();
+      for (int s = s_lo; s < s_hi; ++s) {
+        const int cur = (s - s_lo) & 1;
+        if (s + 1 < s_hi) lstore(cur ^ 1);
+        if (s + 2 < s_hi) gload(s + 2);
+        if (decltype(full)::value || nbv > 0) compute(smem + cur * STAGE, full);
+        __syncthreads();
+      }
+    };
+    if (s_lo < s_hi) {  // an empty group (WGRAD) leaves the accumulators at zero
+      if (nbv == BB)
+        kloop(std::true_type{});
+      else
+        kloop(std::false_type{});
+    }
   }
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
