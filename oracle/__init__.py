@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
                                              i32]
         L.oracle_backward_wsample.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                                               vp, i32]
+        L.oracle_rope.argtypes = [i64, i32, i32, dbl, i64, i32, vp, vp]
+        L.oracle_attention.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, i32]
+        L.oracle_block.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, dbl, dbl, i32, vp, vp, vp, vp, vp, vp,
+                                   vp, vp, i64, vp, vp, vp, vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -249,3 +253,55 @@ def backward_wsample(x, w_gate, w1, w3, w2, K, dy, queries, bias=None, threads=0
     lib().oracle_backward_wsample(T, d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(dy),
                                   q.shape[0], _p(q), _p(val), threads)
     return val
+
+
+# ----------------------------------------------------------------------------- decoder block
+# The block around the MoE layer (formulas and readings in oracle.cpp): pre-norm residual,
+# grouped-query causal attention with rotary positions, then the MoE sub-block.
+
+def rope(x, n_heads, D, base, p0=0):
+    """Rotary embedding of rows x [T][n_heads*D] at positions p0..p0+T-1. Returns float64."""
+    x = _c(x)
+    T = x.shape[0]
+    assert x.shape[1] == n_heads * D and D % 2 == 0
+    out = np.empty((T, n_heads * D), np.float64)
+    lib().oracle_rope(T, n_heads, D, float(base), int(p0), _dtype_code(x), _p(x), _p(out))
+    return out
+
+
+def attention(q, k, v, Hq, Hkv, tokens=None, threads=0):
+    """Causal grouped-query attention. q [T][Hq*D], k, v [T][Hkv*D] (same storage dtype),
+    positions 0..T-1. Returns out [n][Hq*D] float64 for the selected positions."""
+    q, k, v = _c(q), _c(k), _c(v)
+    T = q.shape[0]
+    D = q.shape[1] // Hq
+    dt = _dtype_code(q)
+    assert q.shape == (T, Hq * D) and k.shape == (T, Hkv * D) and v.shape == (T, Hkv * D) and Hq % Hkv == 0
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    out = np.empty((tokens.shape[0], Hq * D), np.float64)
+    lib().oracle_attention(T, Hq, Hkv, D, dt, _p(q), _p(k), _p(v), tokens.shape[0], _p(tokens), _p(out), threads)
+    return out
+
+
+def block(h, w_qkv, w_o, w_gate, w1, w3, w2, K, Hq, Hkv, base, eps, tokens=None, bias=None, threads=0):
+    """One decoder block of a single sequence. h [T][d] float64 (residual stream in), weights as
+    bf16 bit patterns: w_qkv [(Hq+2Hkv)*D][d], w_o [d][Hq*D], MoE weights as in forward().
+    Returns dict(h1, x2, h2, idx, logits) for the selected tokens."""
+    h = _c(h, np.float64)
+    w_qkv, w_o, w_gate, w1, w3, w2 = _c(w_qkv), _c(w_o), _c(w_gate), _c(w1), _c(w3), _c(w2)
+    bias = _c(bias, np.float32)
+    T, d = h.shape
+    E, F, _ = w1.shape
+    D = w_o.shape[1] // Hq
+    for a in (w_qkv, w_o, w_gate, w1, w3, w2):
+        assert a.dtype == np.uint16, "block weights are bf16 bit patterns"
+    assert w_qkv.shape == ((Hq + 2 * Hkv) * D, d) and w_o.shape == (d, Hq * D) and Hq % Hkv == 0
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    n = tokens.shape[0]
+    out = {"h1": np.empty((n, d)), "x2": np.empty((n, d), np.uint16), "h2": np.empty((n, d)),
+           "idx": np.empty((n, K), np.int32), "logits": np.empty((n, E))}
+    lib().oracle_block(T, d, Hq, Hkv, D, F, E, K, float(base), float(eps), 1, _p(h), _p(w_qkv), _p(w_o),
+                       _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n, _p(tokens), _p(out["h1"]), _p(out["x2"]),
+                       _p(out["h2"]), _p(out["idx"]), _p(out["logits"]), threads)
+    return out

@@ -48,6 +48,21 @@
  * The gates of the backward come from the unrounded double logits (the forward
  * above uses fp32-rounded ones, a difference of ~1e-7 relative); the TopK
  * decision is taken on fp32-rounded logits in both.
+ *
+ * Decoder block. The pages give the surrounding transformer only as numbers
+ * (xyznot.com summary, "Método": 32 layers, model width 4096, 32 attention
+ * heads, 8 key-value heads; Mixtral keeps the Mistral 7B architecture and swaps
+ * each feed-forward sub-block for the MoE layer; a full 32k-token context). The
+ * block is read as the pre-norm residual form of that family:
+ *   u  = bf16(h / sqrt(mean(h^2) + eps))                      (unit norm weight, as above)
+ *   q, k, v = u . Wq^T, u . Wk^T, u . Wv^T                     (no biases; W_qkv stacks the three)
+ *   rotary position embedding on q and k: in each head of width D, the pair (i, i + D/2)
+ *   of position p is turned by the angle p * base^(-2i/D)
+ *   per query head hq, with key-value head hq / (Hq/Hkv): causal softmax attention
+ *   o_t = sum_{j<=t} softmax_j(q_t . k_j / sqrt(D)) v_j
+ *   h1 = h + o . Wo^T;   h2 = h1 + MoE(bf16(h1 / sqrt(mean(h1^2) + eps)))
+ * Head width D = 4096/32 = 128 follows from the numbers; the rotary base and the
+ * pair convention are readings (the pages name no position encoding).
  */
 #include <cmath>
 #include <cstdint>
@@ -435,6 +450,142 @@ void oracle_backward_wsample(int64_t T, int d, int F, int E, int K, int dtype, c
       }
     val[u] = acc;
   });
+}
+
+// ----------------------------------------------------------------------------- decoder block
+
+// Rotary position embedding, in place on one head vector x [D] at position p.
+static void rope_head(double* x, int D, int64_t p, double base) {
+  const int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    const double ang = (double)p * std::pow(base, -2.0 * i / D);
+    const double c = std::cos(ang), sn = std::sin(ang);
+    const double a = x[i], b = x[i + half];
+    x[i] = a * c - b * sn;
+    x[i + half] = a * sn + b * c;
+  }
+}
+
+// RoPE of T rows of n_heads heads (row t = position p0 + t): in [T][n_heads*D] (storage dtype),
+// out [T][n_heads*D] double.
+void oracle_rope(int64_t T, int n_heads, int D, double base, int64_t p0, int dtype, const void* in, double* out) {
+  const int64_t W = (int64_t)n_heads * D;
+  for (int64_t t = 0; t < T; ++t)
+    for (int h = 0; h < n_heads; ++h) {
+      double* x = out + t * W + (int64_t)h * D;
+      for (int i = 0; i < D; ++i) x[i] = load(in, dtype, t * W + (int64_t)h * D + i);
+      rope_head(x, D, p0 + t, base);
+    }
+}
+
+// Causal grouped-query attention for selected positions: q [T][Hq*D], k, v [T][Hkv*D] (storage
+// dtype), query head hq reads key-value head hq / (Hq/Hkv); out [n_sel][Hq*D] double.
+void oracle_attention(int64_t T, int Hq, int Hkv, int D, int dtype, const void* q, const void* k, const void* v,
+                      int64_t n_sel, const int64_t* tok_sel, double* out, int threads) {
+  (void)T;
+  const int G = Hq / Hkv;
+  const double scale = 1.0 / std::sqrt((double)D);
+  parallel_for(n_sel * Hq, threads, [&](int64_t u) {
+    const int64_t i = u / Hq, t = tok_sel[i];
+    const int hq = (int)(u % Hq), hk = hq / G;
+    std::vector<double> s(t + 1);
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= t; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < D; ++c)
+        acc += load(q, dtype, t * Hq * D + (int64_t)hq * D + c) * load(k, dtype, j * Hkv * D + (int64_t)hk * D + c);
+      s[j] = acc * scale;
+      m = std::max(m, s[j]);
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j <= t; ++j) {
+      s[j] = std::exp(s[j] - m);
+      z += s[j];
+    }
+    double* o = out + i * Hq * D + (int64_t)hq * D;
+    for (int c = 0; c < D; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j <= t; ++j) {
+      const double p = s[j] / z;
+      for (int c = 0; c < D; ++c) o[c] += p * load(v, dtype, j * Hkv * D + (int64_t)hk * D + c);
+    }
+  });
+}
+
+// One decoder block for selected tokens of a single sequence of T tokens (positions 0..T-1):
+// h [T][d] double (the residual stream entering the block), w_qkv [(Hq+2Hkv)*D][d] and
+// w_o [d][Hq*D] in storage dtype (bf16 or fp32, as the MoE weights). Returns for the selected
+// tokens h1 [n_sel][d] (after attention), x2 [n_sel][d] (bf16 bits of the MoE input) and
+// h2 [n_sel][d] (after the MoE), plus the routing of x2 (idx [n_sel][K], logits [n_sel][E]).
+// Rows 0..max(tok_sel) are projected to keys and values, as causal attention needs them.
+void oracle_block(int64_t T, int d, int Hq, int Hkv, int D, int F, int E, int K, double base, double eps,
+                  int dtype, const double* h, const void* w_qkv, const void* w_o, const void* w_gate,
+                  const float* bias, const void* w1, const void* w3, const void* w2, int64_t n_sel,
+                  const int64_t* tok_sel, double* h1_sel, uint16_t* x2_sel, double* h2_sel, int32_t* idx_sel,
+                  double* logits_sel, int threads) {
+  (void)T;
+  int64_t n = 0;  // rows needed: 0..max selected position
+  for (int64_t i = 0; i < n_sel; ++i) n = std::max<int64_t>(n, tok_sel[i] + 1);
+  const int64_t Wq = (int64_t)Hq * D, Wk = (int64_t)Hkv * D;
+  std::vector<uint16_t> u((size_t)n * d);
+  oracle_rmsnorm_bf16(n, d, eps, h, u.data(), nullptr);
+  // keys and values of every needed row, queries of the selected rows (double, after RoPE)
+  std::vector<double> kk((size_t)n * Wk), vv((size_t)n * Wk), qq((size_t)n_sel * Wq);
+  auto proj = [&](int64_t t, int64_t row0, int64_t nrows, double* dst) {
+    for (int64_t r = 0; r < nrows; ++r) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += load(w_qkv, dtype, (row0 + r) * d + c) * load(u.data(), 1, t * d + c);
+      dst[r] = acc;
+    }
+  };
+  parallel_for(n, threads, [&](int64_t t) {
+    proj(t, Wq, Wk, kk.data() + t * Wk);
+    proj(t, Wq + Wk, Wk, vv.data() + t * Wk);
+    for (int hk = 0; hk < Hkv; ++hk) rope_head(kk.data() + t * Wk + (int64_t)hk * D, D, t, base);
+  });
+  parallel_for(n_sel, threads, [&](int64_t i) {
+    const int64_t t = tok_sel[i];
+    proj(t, 0, Wq, qq.data() + i * Wq);
+    for (int hq = 0; hq < Hq; ++hq) rope_head(qq.data() + i * Wq + (int64_t)hq * D, D, t, base);
+  });
+  // attention of the selected rows (queries stored compactly: pass positions through a remap)
+  std::vector<double> o((size_t)n_sel * Wq);
+  const int G = Hq / Hkv;
+  const double scale = 1.0 / std::sqrt((double)D);
+  parallel_for(n_sel * Hq, threads, [&](int64_t uu) {
+    const int64_t i = uu / Hq, t = tok_sel[i];
+    const int hq = (int)(uu % Hq), hk = hq / G;
+    std::vector<double> s(t + 1);
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= t; ++j) {
+      double acc = 0.0;
+      for (int c = 0; c < D; ++c) acc += qq[i * Wq + (int64_t)hq * D + c] * kk[j * Wk + (int64_t)hk * D + c];
+      s[j] = acc * scale;
+      m = std::max(m, s[j]);
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j <= t; ++j) {
+      s[j] = std::exp(s[j] - m);
+      z += s[j];
+    }
+    double* oo = o.data() + i * Wq + (int64_t)hq * D;
+    for (int c = 0; c < D; ++c) oo[c] = 0.0;
+    for (int64_t j = 0; j <= t; ++j)
+      for (int c = 0; c < D; ++c) oo[c] += s[j] / z * vv[j * Wk + (int64_t)hk * D + c];
+  });
+  // output projection and residual, then the MoE sub-block on the selected rows
+  for (int64_t i = 0; i < n_sel; ++i)
+    for (int r = 0; r < d; ++r) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < Wq; ++c) acc += load(w_o, dtype, (int64_t)r * Wq + c) * o[i * Wq + c];
+      h1_sel[i * d + r] = h[tok_sel[i] * d + r] + acc;
+    }
+  oracle_rmsnorm_bf16(n_sel, d, eps, h1_sel, x2_sel, nullptr);
+  std::vector<int64_t> all(n_sel);
+  for (int64_t i = 0; i < n_sel; ++i) all[i] = i;
+  std::vector<double> y((size_t)n_sel * d), w((size_t)n_sel * K);
+  oracle_forward(n_sel, d, F, E, K, 1, x2_sel, w_gate, bias, w1, w3, w2, n_sel, all.data(), y.data(), logits_sel,
+                 idx_sel, w.data(), threads);
+  for (int64_t i = 0; i < n_sel * d; ++i) h2_sel[i] = h1_sel[i] + y[i];
 }
 
 }  // extern "C"
