@@ -21,7 +21,8 @@
  *     moe_expert_ffn  grouped SwiGLU expert FFN over expert-contiguous rows
  *     moe_combine     gate-weighted sum back in token order
  *     moe_forward     all of the above in one call
- * and moe_backward computes the gradients of the layer.
+ * and moe_backward computes the gradients of the layer; moe_attention and moe_block_forward run
+ * the decoder block the layer sits in (below).
  *
  * Conventions shared by every call
  *  - Tensors are DEVICE pointers (hipMalloc'ed or torch CUDA/HIP tensors),
@@ -212,6 +213,54 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
  * do not describe the norm; unit weight): x_bf16[t] = bf16(h[t] / sqrt(mean_j h[t][j]^2 + eps)),
  * rounded to nearest even. h [T][d] fp32 in, x_bf16 [T][d] bf16 out. */
 moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Decoder block around the layer. The pages give the rest of the transformer by its numbers only
+ * (xyznot.com summary, "Método": 32 layers of width 4096, 32 attention heads, 8 key-value heads;
+ * Mixtral keeps the Mistral 7B architecture and replaces each feed-forward sub-block by the
+ * mixture-of-experts layer; a full 32k-token context). This library reads the block as the
+ * pre-norm residual form of that architecture, for one sequence of T positions 0..T-1:
+ *     u  = bf16(rmsnorm(h))                      (unit weight, eps as given)
+ *     [q | k | v] = u . W_qkv^T                   (no biases)
+ *     q, k: rotary embedding, in each head of width D the pair (i, i + D/2) of position p turns by
+ *           the angle p * rope_base^(-2i/D)
+ *     o_t = sum_{j<=t} softmax_j(q_t . k_j / sqrt(D)) v_j per query head; query head h reads
+ *           key-value head h / (n_heads / n_kv_heads)
+ *     h  += o . W_o^T;     h += MoE(bf16(rmsnorm(h)))
+ * The rotary form and its base are readings (the pages name no position encoding).
+ * Precision: bf16 operands of every product, fp32 sums; q, k, v, the attention weights and o are
+ * rounded to bf16 (nearest even); h stays fp32. */
+typedef struct {
+  int64_t T;          /* positions of the sequence */
+  int32_t d;          /* model width (the residual stream) */
+  int32_t n_heads;    /* query heads */
+  int32_t n_kv_heads; /* key-value heads; n_heads / n_kv_heads must be a multiple of 4 */
+  int32_t head_dim;   /* D; 128 is supported */
+  float rope_base;    /* base of the rotary angles (> 1) */
+  float eps;          /* RMS norm epsilon (>= 0) */
+} moe_attn_dims;
+
+/* Causal grouped-query attention (the o_t line above):
+ *   q [n_heads][T][D], k, v [n_kv_heads][T][D] bf16 in (q and k already rotated),
+ *   o [T][n_heads * D] bf16 out (token-major, the input of the output projection).
+ * Supported: head_dim = 128, n_heads a multiple of 4 * n_kv_heads. */
+moe_status moe_attention(const moe_attn_dims* attn, const void* q, const void* k, const void* v, void* o,
+                         void* stream);
+
+/* One decoder block, in place on the fp32 residual stream h [T][d]:
+ *   w_qkv [(n_heads + 2 n_kv_heads) * D][d] bf16, row-major (rows: the q heads, then k, then v)
+ *   w_o   [d][n_heads * D] bf16, row-major
+ *   w_gate, w1, w3, w2: the layer's weights as for moe_forward (dims->dtype must be MOE_BF16)
+ *   moe->T and moe->d must equal attn->T and attn->d. opts: gate_bias and stage_events as for
+ *   moe_forward (the events time the mixture-of-experts stages); y_dtype and accumulate are
+ *   ignored (the layer's output is added to h).
+ *   workspace: >= moe_block_workspace_bytes() bytes of device memory, 256-byte aligned.
+ * Supported: bf16, head_dim 128, n_heads a multiple of 4 * n_kv_heads, d a multiple of 256
+ * (with the layer's limits). */
+size_t moe_block_workspace_bytes(const moe_dims* moe, const moe_attn_dims* attn);
+moe_status moe_block_forward(const moe_dims* moe, const moe_attn_dims* attn, const moe_opts* opts, float* h,
+                             const void* w_qkv, const void* w_o, const void* w_gate, const void* w1, const void* w3,
+                             const void* w2, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* moe_status_string(moe_status s);

@@ -149,6 +149,62 @@ moe_status check_backward_sizes(const moe_dims& m) {
 
 const moe_opts kDefaultOpts = {nullptr, -1, 0, nullptr};
 
+moe_status check_attn(const moe_attn_dims* a) {
+  if (!a) return fail(MOE_ERR_INVALID_ARG, "attn is NULL");
+  if (a->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld is negative", (long long)a->T);
+  if (a->d <= 0 || a->n_heads <= 0 || a->n_kv_heads <= 0 || a->head_dim <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "d, n_heads, n_kv_heads and head_dim must be positive");
+  if (a->n_heads % a->n_kv_heads != 0)
+    return fail(MOE_ERR_INVALID_ARG, "n_heads = %d is not a multiple of n_kv_heads = %d", a->n_heads, a->n_kv_heads);
+  if (!(a->rope_base > 1.0f)) return fail(MOE_ERR_INVALID_ARG, "rope_base must be > 1");
+  if (!(a->eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+  if (a->head_dim != 128) return fail(MOE_ERR_UNSUPPORTED, "head_dim = %d (128 is supported)", a->head_dim);
+  if ((a->n_heads / a->n_kv_heads) % 4 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "n_heads / n_kv_heads = %d must be a multiple of 4",
+                a->n_heads / a->n_kv_heads);
+  if (a->T >= (int64_t(1) << 31) / 4) return fail(MOE_ERR_UNSUPPORTED, "T must be < 2^29");
+  return MOE_OK;
+}
+
+// Block workspace: the layer's own workspace first, then the block's buffers.
+struct BlockWorkspace {
+  size_t moe, offsets, u, qkv, q, k, v, o, a, x2, total;
+};
+
+BlockWorkspace block_layout(const moe_dims& m, const moe_attn_dims& at) {
+  const size_t T = (size_t)at.T, d = (size_t)at.d, D = (size_t)at.head_dim;
+  const size_t Hq = (size_t)at.n_heads, Hkv = (size_t)at.n_kv_heads;
+  BlockWorkspace w{};
+  size_t o = 0;
+  auto take = [&](size_t& field, size_t bytes) {
+    field = o;
+    o = align256(o + bytes);
+  };
+  take(w.moe, layout(m).total);
+  take(w.offsets, 2 * 4);
+  take(w.u, T * d * 2);
+  take(w.qkv, T * (Hq + 2 * Hkv) * D * 4);
+  take(w.q, Hq * T * D * 2);
+  take(w.k, Hkv * T * D * 2);
+  take(w.v, Hkv * T * D * 2);
+  take(w.o, T * Hq * D * 2);
+  take(w.a, T * d * 4);
+  take(w.x2, T * d * 2);
+  w.total = o;
+  return w;
+}
+
+moe_status check_block(const moe_dims* dims, const moe_attn_dims* attn) {
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT));
+  MOE_TRY(check_attn(attn));
+  if (dims->T != attn->T || dims->d != attn->d)
+    return fail(MOE_ERR_INVALID_ARG, "moe (T = %lld, d = %d) and attn (T = %lld, d = %d) disagree",
+                (long long)dims->T, dims->d, (long long)attn->T, attn->d);
+  if (dims->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the decoder block supports bf16 only");
+  if (attn->d % 256 != 0) return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 256", attn->d);
+  return MOE_OK;
+}
+
 moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
   const moe_opts& op = o ? *o : kDefaultOpts;
   if (op.accumulate != 0 && op.accumulate != 1)
@@ -165,7 +221,7 @@ moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -435,6 +491,67 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   moe::launch_tile_wgrad(dab + m.F, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw3, s);
   moe::launch_tile_wgrad(at(L.do_perm), m.d, m.d, at(L.h), m.F, m.F, offsets, m.E, dw2, s);
   return check_launch("moe_backward (weight gradients)");
+}
+
+moe_status moe_attention(const moe_attn_dims* attn, const void* q, const void* k, const void* v, void* o,
+                         void* stream) {
+  MOE_TRY(check_attn(attn));
+  MOE_TRY(check_ptr(q, "q"));
+  MOE_TRY(check_ptr(k, "k"));
+  MOE_TRY(check_ptr(v, "v"));
+  MOE_TRY(check_ptr(o, "o"));
+  if (attn->T == 0) return MOE_OK;
+  moe::launch_attention(q, k, v, o, attn->T, attn->n_heads, attn->n_kv_heads, static_cast<hipStream_t>(stream));
+  return check_launch("moe_attention");
+}
+
+size_t moe_block_workspace_bytes(const moe_dims* dims, const moe_attn_dims* attn) {
+  if (check_block(dims, attn) != MOE_OK) return 0;
+  return block_layout(*dims, *attn).total;
+}
+
+moe_status moe_block_forward(const moe_dims* dims, const moe_attn_dims* attn, const moe_opts* opts, float* h,
+                             const void* w_qkv, const void* w_o, const void* w_gate, const void* w1, const void* w3,
+                             const void* w2, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_block(dims, attn));
+  MOE_TRY(check_ptr(h, "h"));
+  MOE_TRY(check_ptr(w_qkv, "w_qkv"));
+  MOE_TRY(check_ptr(w_o, "w_o"));
+  MOE_TRY(check_ptr(w_gate, "w_gate"));
+  MOE_TRY(check_ptr(w1, "w1"));
+  MOE_TRY(check_ptr(w3, "w3"));
+  MOE_TRY(check_ptr(w2, "w2"));
+  const moe_attn_dims& at = *attn;
+  if (at.T == 0) return MOE_OK;
+  const BlockWorkspace L = block_layout(*dims, at);
+  MOE_TRY(check_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  auto at_ = [&](size_t off) { return static_cast<void*>(ws + off); };
+  int32_t* off = static_cast<int32_t*>(at_(L.offsets));
+  float* qkv = static_cast<float*>(at_(L.qkv));
+  float* a = static_cast<float*>(at_(L.a));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = at.head_dim, Hq = at.n_heads, Hkv = at.n_kv_heads;
+  const int rm = MOE_LAYOUT_ROWMAJOR;
+
+  // attention sub-block: the two dense products run on the grouped kernels with one group of T rows
+  moe::launch_set_offsets(off, at.T, s);
+  moe::launch_rmsnorm(h, at.T, at.d, at.eps, at_(L.u), s);
+  moe::launch_expert_down(MOE_BF16, rm, at_(L.u), off, at.T, (Hq + 2 * Hkv) * D, at.d, 1, w_qkv, qkv, 1, nullptr, s);
+  moe::launch_rope_qkv(qkv, at.T, Hq, Hkv, (double)at.rope_base, at_(L.q), at_(L.k), at_(L.v), s);
+  moe::launch_attention(at_(L.q), at_(L.k), at_(L.v), at_(L.o), at.T, Hq, Hkv, s);
+  moe::launch_expert_down(MOE_BF16, rm, at_(L.o), off, at.T, at.d, Hq * D, 1, w_o, a, 1, nullptr, s);
+  moe::launch_residual_norm(h, a, at.T, at.d, at.eps, at_(L.x2), s);
+  MOE_TRY(check_launch("moe_block_forward (attention)"));
+  // mixture-of-experts sub-block, added to the residual stream
+  moe_opts o2 = opts ? *opts : kDefaultOpts;
+  o2.accumulate = 1;
+  o2.y_dtype = MOE_F32;
+  return moe_forward(dims, &o2, at_(L.x2), w_gate, w1, w3, w2, h, at_(L.moe), layout(*dims).total, stream);
 }
 
 moe_status moe_rmsnorm(int64_t T, int32_t d, float eps, const float* h, void* x_bf16, void* stream) {

@@ -1,0 +1,296 @@
+// Decoder block around the mixture-of-experts layer: rotary embedding, causal grouped-query
+// attention and the residual + norm step. The pages give the block by its numbers only (xyznot.com
+// summary, "Método": 32 attention heads, 8 key-value heads, width 4096, the Mistral 7B layout with
+// the MoE layer in place of the feed-forward sub-block, a full 32k context); head width 128 and
+// the rotary form are readings (no position encoding is named on the pages).
+//
+// Attention (flash form, one pass over the keys with a running softmax): a workgroup takes 64
+// query positions of the 4 query heads that share one key-value head (group size Hq/Hkv a
+// multiple of 4), one wavefront per head, so every 64-key tile staged in LDS serves 4 heads.
+// Per wavefront and key tile, on 16x16x32 bf16 MFMAs with fp32 sums:
+//   S^T = K Q^T       (K from LDS, the wavefront's Q fragments held in registers all along)
+//   running max / sum per query, P = exp(S - max) rounded to bf16
+//   O^T += V^T P^T    (V^T assembled by transposing LDS reads, P^T straight from the S^T
+//                      accumulators: the contraction order over keys is chosen to match the
+//                      layout in which the accumulators hold them)
+// Query positions are the output columns of both products, so every softmax statistic lives in
+// the four lanes that hold one column (two cross-lane steps). Query blocks are launched longest
+// first (a block at position p visits p/64 + 1 key tiles).
+#include "common.hpp"
+#include "launch.hpp"
+
+#include <cmath>
+
+namespace moe {
+namespace {
+
+constexpr int kHD = 128;         // head width
+constexpr int kQB = 64;          // query positions per workgroup (per wavefront)
+constexpr int kKB = 64;          // keys per tile
+constexpr int kKRow = kHD + 8;   // LDS row of the K tile (elements): 272 B, conflict-free 16 B reads
+constexpr int kVRow = kHD + 16;  // LDS row of the V tile: 288 B, conflict-free transposing reads
+
+// qkv [T][(Hq + 2 Hkv) * 128] fp32 -> q [Hq][T][128], k [Hkv][T][128], v [Hkv][T][128] bf16, with the
+// rotary embedding on q and k: in each head the pair (i, i + 64) of position t turns by the angle
+// t * base^(-i/64). One wavefront per (position, head); lane i owns the pair (i, i + 64).
+__global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__ qkv, int64_t T, int Hq, int Hkv,
+                                                       double log_base, bf16_t* __restrict__ q,
+                                                       bf16_t* __restrict__ k, bf16_t* __restrict__ v) {
+  const int lane = threadIdx.x & 63;
+  const int H = Hq + 2 * Hkv;
+  const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (item >= T * H) return;
+  const int64_t t = item / H;
+  const int h = (int)(item - t * H);
+  const float* src = qkv + t * (int64_t)H * kHD + (int64_t)h * kHD;
+  float a = src[lane], b = src[lane + 64];
+  bf16_t* dst;
+  if (h < Hq + Hkv) {
+    // angle in double, reduced to [-pi, pi] before the fp32 sine and cosine
+    const double ang = (double)t * exp(-(double)lane / 64.0 * log_base);
+    const double red = ang - 6.283185307179586 * rint(ang / 6.283185307179586);
+    float sn, cs;
+    sincosf((float)red, &sn, &cs);
+    const float ra = a * cs - b * sn, rb = a * sn + b * cs;
+    a = ra;
+    b = rb;
+    dst = h < Hq ? q + ((int64_t)h * T + t) * kHD : k + ((int64_t)(h - Hq) * T + t) * kHD;
+  } else {
+    dst = v + ((int64_t)(h - Hq - Hkv) * T + t) * kHD;
+  }
+  dst[lane] = (bf16_t)f32_to_bf16_rne(a);
+  dst[lane + 64] = (bf16_t)f32_to_bf16_rne(b);
+}
+
+__device__ inline float max4(f32x4_t v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+// q [Hq][T][128], k, v [Hkv][T][128] bf16 -> o [T][Hq*128] bf16. Grid: (T/64 rounded up) * (Hq/4)
+// workgroups of 4 wavefronts.
+__global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                           const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
+                                                           int64_t T, int Hq, int Hkv, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) bf16_t ks[2][kKB * kKRow];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[2][kKB * kVRow];
+
+  const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nqb = (int)((T + kQB - 1) / kQB), nhg = Hq / 4;
+  const int qb = nqb - 1 - (int)(blockIdx.x / nhg);  // longest blocks first
+  const int hq = (int)(blockIdx.x % nhg) * 4 + wave;
+  const int hk = (hq / (Hq / Hkv));  // the 4 heads of a workgroup share it (group size % 4 == 0)
+  const int64_t q0 = (int64_t)qb * kQB;
+
+  // Q fragments as the B operand of S^T = K Q^T: query block j, k-chunk c (32 dims); lane: query
+  // q0 + 16 j + li, dims 32 c + 8 g .. +7. Rows past T load the last row (never stored).
+  u32x4_t qf[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = min(q0 + 16 * j + li, T - 1);
+    const bf16_t* row = q + ((int64_t)hq * T + t) * kHD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[j][c] = load16(row + 32 * c + 8 * g);
+  }
+
+  // K/V tile loads: 64 rows x 256 B each, 16 B per thread per round, 4 rounds per tile
+  const bf16_t* kbase = k + (int64_t)hk * T * kHD;
+  const bf16_t* vbase = v + (int64_t)hk * T * kHD;
+  const int lr = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 8;  // row (of 16) and column of this thread
+  u32x4_t kreg[4], vreg[4];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = min(k0 + lr + 16 * r, T - 1);  // keys past T are masked below
+      kreg[r] = load16(kbase + key * kHD + lc);
+      vreg[r] = load16(vbase + key * kHD + lc);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      store16(&ks[buf][(lr + 16 * r) * kKRow + lc], kreg[r]);
+      store16(&vs[buf][(lr + 16 * r) * kVRow + lc], vreg[r]);
+    }
+  };
+
+  f32x4_t oacc[8][4];  // O^T: dim block db (16 dims) x query block j
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) oacc[d][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[4], lrun[4];  // running max (all four lanes of a query agree) and this lane's partial sum
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mrun[j] = -INFINITY;
+    lrun[j] = 0.f;
+  }
+
+  const int nsteps = qb + 1;  // key tiles 0..qb; the last one is the diagonal tile
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    const int64_t k0 = (int64_t)st * kKB;
+    if (st + 1 < nsteps) gload(k0 + kKB);
+
+    // S^T = K Q^T: key block i (A operand rows = keys, from LDS), query block j
+    f32x4_t s[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4_t kf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = load16(&ks[buf][(16 * i + li) * kKRow + 32 * c + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[i][j] = mfma_bf16(kf[i], qf[j][c], s[i][j]);
+    }
+    // causal mask on the diagonal tile (k0 == q0), which also holds every key past T
+    if (st == nsteps - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kk = 16 * i + 4 * g + r, qq = 16 * j + li;
+            if (kk > qq || k0 + kk >= T) s[i][j][r] = -INFINITY;
+          }
+    }
+    // running softmax per query column; P^T as the B operand of the second product: key chunk kc
+    // (32 keys = key blocks 2kc, 2kc+1), lane slots 0-3 = keys 4g..4g+3 of block 2kc, slots 4-7 the
+    // same of block 2kc+1
+    u32x4_t pf[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mnew = fmaxf(mrun[j], mx);
+      const float alpha = exp2f((mrun[j] - mnew) * scale_log2);
+      mrun[j] = mnew;
+      const float mb = mnew * scale_log2;
+      float p[4][4], sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[i][r] = exp2f(fmaf(s[i][j][r], scale_log2, -mb));
+          sum += p[i][r];
+        }
+      lrun[j] = lrun[j] * alpha + sum;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        pf[kc][j] = u32x4_t{pack_bf16x2(p[2 * kc][0], p[2 * kc][1]), pack_bf16x2(p[2 * kc][2], p[2 * kc][3]),
+                            pack_bf16x2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
+                            pack_bf16x2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
+    }
+    // O^T += V^T P^T: A operand (dims x keys) by transposing reads of the V tile: in each group of
+    // 16 lanes, lanes 4a..4a+3 address row a's 16 columns and lane i receives column i of the 4
+    // rows, so lane (g, i) gets dim 16 db + i at keys 4g..4g+3 of key blocks 2kc and 2kc+1
+    typedef __attribute__((ext_vector_type(4))) short v4s;
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const int ta = (lane >> 2) & 3, tc = lane & 3;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const bf16_t* p0 = &vs[buf][(32 * kc + 4 * g + ta) * kVRow + 16 * d + 4 * tc];
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p0));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p0 + 16 * kVRow));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oacc[d][j] = mfma_bf16(vf, pf[kc][j], oacc[d][j]);
+      }
+    // the other buffer was last read in the previous step, before the barrier that ended it
+    if (st + 1 < nsteps) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // O = O^T / sum, rounded to bf16; lane: query q0 + 16 j + li, dims 16 db + 4 g .. +3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float l = lrun[j];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = 1.0f / l;
+    const int64_t t = q0 + 16 * j + li;
+    if (t >= T) continue;
+    bf16_t* dst = o + t * (int64_t)Hq * kHD + (int64_t)hq * kHD + 4 * g;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<u32x2_t*>(dst + 16 * d) =
+          u32x2_t{pack_bf16x2(oacc[d][j][0] * inv, oacc[d][j][1] * inv),
+                  pack_bf16x2(oacc[d][j][2] * inv, oacc[d][j][3] * inv)};
+  }
+}
+
+// h[t] += a[t] (fp32), then x[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps)); one wavefront per row.
+__global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ h, const float* __restrict__ a,
+                                                            int64_t T, int d, float eps, bf16_t* __restrict__ x) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  float* row = h + t * d;
+  const float* add = a + t * d;
+  float ss = 0.0f;
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+    v += *reinterpret_cast<const f32x4_t*>(add + c);
+    *reinterpret_cast<f32x4_t*>(row + c) = v;
+    ss = fmaf(v[0], v[0], ss);
+    ss = fmaf(v[1], v[1], ss);
+    ss = fmaf(v[2], v[2], ss);
+    ss = fmaf(v[3], v[3], ss);
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane * 4; c < d; c += kWave * 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+    *reinterpret_cast<u32x2_t*>(x + t * d + c) = u32x2_t{pack_bf16x2(v[0] * inv, v[1] * inv),
+                                                         pack_bf16x2(v[2] * inv, v[3] * inv)};
+  }
+}
+
+__global__ void set_offsets_kernel(int32_t* off, int32_t T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+}  // namespace
+
+void launch_rope_qkv(const float* qkv, int64_t T, int Hq, int Hkv, double base, void* q, void* k, void* v,
+                     hipStream_t s) {
+  const int64_t items = T * (Hq + 2 * Hkv);
+  launch_kernel(rope_qkv_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, qkv, T, Hq, Hkv, std::log(base),
+                static_cast<bf16_t*>(q), static_cast<bf16_t*>(k), static_cast<bf16_t*>(v));
+}
+
+void launch_attention(const void* q, const void* k, const void* v, void* o, int64_t T, int Hq, int Hkv,
+                      hipStream_t s) {
+  const int64_t nqb = (T + kQB - 1) / kQB;
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHD));
+  launch_kernel(attention_kernel, dim3((unsigned)(nqb * (Hq / 4))), dim3(256), 0, s, static_cast<const bf16_t*>(q),
+                static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<bf16_t*>(o), T, Hq, Hkv,
+                scale_log2);
+}
+
+void launch_residual_norm(float* h, const float* a, int64_t T, int d, float eps, void* x, hipStream_t s) {
+  launch_kernel(residual_norm_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, a, T, d, eps,
+                static_cast<bf16_t*>(x));
+}
+
+void launch_set_offsets(int32_t* off, int64_t T, hipStream_t s) {
+  launch_kernel(set_offsets_kernel, dim3(1), dim3(64), 0, s, off, (int32_t)T);
+}
+
+}  // namespace moe

@@ -111,4 +111,16 @@ int dwgate_chunks(int64_t T);
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg,
                    hipStream_t stream);
 
+// Decoder block (attention.hip). Head width 128; a key-value head serves a multiple of 4 query heads.
+// qkv [T][(Hq + 2 Hkv) * 128] fp32 -> q [Hq][T][128], k, v [Hkv][T][128] bf16, rotary embedding on q, k.
+void launch_rope_qkv(const float* qkv, int64_t T, int Hq, int Hkv, double base, void* q, void* k, void* v,
+                     hipStream_t stream);
+// Causal grouped-query attention: q [Hq][T][128], k, v [Hkv][T][128] -> o [T][Hq * 128], all bf16.
+void launch_attention(const void* q, const void* k, const void* v, void* o, int64_t T, int Hq, int Hkv,
+                      hipStream_t stream);
+// h += a (fp32), x = bf16(rmsnorm(h)) (unit weight).
+void launch_residual_norm(float* h, const float* a, int64_t T, int d, float eps, void* x, hipStream_t stream);
+// off = {0, T}: one group holding every row (dense products through the grouped kernels).
+void launch_set_offsets(int32_t* off, int64_t T, hipStream_t stream);
+
 }  // namespace moe

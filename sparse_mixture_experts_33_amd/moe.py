@@ -23,8 +23,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 
 # every symbol include/moe.h declares
 SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_workspace_bytes",
-           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_rmsnorm", "moe_status_string",
-           "moe_last_error", "moe_abi_version")
+           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_rmsnorm", "moe_attention",
+           "moe_block_workspace_bytes", "moe_block_forward", "moe_status_string", "moe_last_error",
+           "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -41,6 +42,26 @@ class moe_dims(ctypes.Structure):
 class moe_opts(ctypes.Structure):
     _fields_ = [("gate_bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
                 ("stage_events", ctypes.c_void_p)]
+
+
+class moe_attn_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("eps", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class AttnDims:
+    T: int
+    d: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int = 128
+    rope_base: float = 1e6
+    eps: float = 1e-5
+
+    def c(self) -> moe_attn_dims:
+        return moe_attn_dims(self.T, self.d, self.n_heads, self.n_kv_heads, self.head_dim, self.rope_base, self.eps)
 
 
 @dataclass(frozen=True)
@@ -82,12 +103,17 @@ def lib() -> ctypes.CDLL:
         L.moe_backward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    vp]
         L.moe_rmsnorm.argtypes = [i64, i32, f32, vp, vp, vp]
+        L.moe_attention.argtypes = [P(moe_attn_dims), vp, vp, vp, vp, vp]
+        L.moe_block_workspace_bytes.argtypes = [P(moe_dims), P(moe_attn_dims)]
+        L.moe_block_workspace_bytes.restype = sz
+        L.moe_block_forward.argtypes = [P(moe_dims), P(moe_attn_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, vp,
+                                        sz, vp]
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_forward",
-                     "moe_backward", "moe_rmsnorm"):
+                     "moe_backward", "moe_rmsnorm", "moe_attention", "moe_block_forward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +216,27 @@ def moe_backward(dims: Dims, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, d
 
 def moe_rmsnorm(T: int, d: int, eps: float, h, x_bf16, stream=None):
     _check(lib().moe_rmsnorm(T, d, eps, _ptr(h), _ptr(x_bf16), _stream(stream)))
+
+
+def moe_attention(attn: AttnDims, q, k, v, o, stream=None):
+    """q [n_heads][T][128], k, v [n_kv_heads][T][128] bf16 -> o [T][n_heads*128] bf16."""
+    _check(lib().moe_attention(ctypes.byref(attn.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream)))
+
+
+def moe_block_workspace_bytes(dims: Dims, attn: AttnDims) -> int:
+    return int(lib().moe_block_workspace_bytes(ctypes.byref(dims.c()), ctypes.byref(attn.c())))
+
+
+def moe_block_forward(dims: Dims, attn: AttnDims, h, w_qkv, w_o, w_gate, w1, w3, w2, workspace, gate_bias=None,
+                      stream=None, workspace_bytes=None, stage_events=None):
+    """One decoder block in place on the fp32 residual stream h [T][d] (include/moe.h)."""
+    o = _opts(gate_bias, None, True, dims.dtype,
+              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p).value)
+    nbytes = workspace_bytes if workspace_bytes is not None else (
+        workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
+    _check(lib().moe_block_forward(ctypes.byref(dims.c()), ctypes.byref(attn.c()), ctypes.byref(o), _ptr(h),
+                                   _ptr(w_qkv), _ptr(w_o), _ptr(w_gate), _ptr(w1), _ptr(w3), _ptr(w2),
+                                   _ptr(workspace), nbytes, _stream(stream)))
 
 
 def moe_status_string(status: int) -> str:

@@ -1,0 +1,136 @@
+"""GPU parity of the decoder block (moe_attention, moe_block_forward) against the oracle.
+
+Bars: max|d| / max|ref| <= 2e-2 (the bf16 bar of the layer) for the attention output and for the
+block's update of the residual stream (h_out - h_in). Expected errors are ~5e-3: q, k, v, the
+attention weights and o are rounded to bf16 on the GPU, the oracle keeps double. Tokens whose
+MoE routing has a near-tie between the K-th and (K+1)-th logits are left out of the block
+comparison (a rounding difference upstream may pick the other expert; both are correct).
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from helpers import dev, gaps, host, rel_err, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TIE = 1e-2
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_mixture_experts_33_amd as moe
+    moe.lib()
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return moe
+
+
+def head_major(a, H, T):
+    """[T][H*128] -> [H][T][128] (contiguous)."""
+    return np.ascontiguousarray(a.reshape(T, H, 128).transpose(1, 0, 2))
+
+
+def gpu_attention(M, w, A):
+    T, Hq, Hkv = w.T, w.n_heads, w.n_kv_heads
+    o = torch.empty((T, Hq * 128), dtype=torch.bfloat16, device="cuda")
+    M.moe_attention(M.AttnDims(T, w.d, Hq, Hkv), dev(head_major(A["q"], Hq, T)), dev(head_major(A["k"], Hkv, T)),
+                    dev(head_major(A["v"], Hkv, T)), o)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+ATTN_CASES = {
+    # ragged lengths around the 64-position blocks, one and two query groups per key-value head
+    "T1": dict(T=1, Hq=8, Hkv=2),
+    "T37": dict(T=37, Hq=8, Hkv=2),
+    "T64": dict(T=64, Hq=4, Hkv=1),
+    "T200_g8": dict(T=200, Hq=8, Hkv=1),
+    "T577": dict(T=577, Hq=8, Hkv=2),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_attention_small(M, name):
+    c = ATTN_CASES[name]
+    w = mi.Workload(f"attn_{name}", T=c["T"], d=256, F=256, n_heads=c["Hq"], n_kv_heads=c["Hkv"],
+                    seed=900 + c["T"])
+    say(f"[attention] {name} T={w.T} Hq={w.n_heads} Hkv={w.n_kv_heads}")
+    A = mi.attention_inputs(w)
+    got = gpu_attention(M, w, A)
+    ref = oracle.attention(A["q"], A["k"], A["v"], w.n_heads, w.n_kv_heads)
+    err = rel_err(got, ref)
+    say(f"  max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL
+
+
+def test_attention_is_deterministic(M):
+    w = mi.Workload("attn_det", T=300, d=256, F=256, n_heads=8, n_kv_heads=2, seed=931)
+    A = mi.attention_inputs(w)
+    assert np.array_equal(gpu_attention(M, w, A), gpu_attention(M, w, A))
+
+
+def test_attention_mixtral_heads_sampled(M):
+    """Mixtral's heads (32 query, 8 key-value, width 128) over 4096 positions; the oracle checks
+    sampled positions (first, last, both sides of block edges)."""
+    w = mi.Workload("attn_full", T=4096, d=4096, F=256, seed=932)
+    say(f"[attention] full T={w.T} Hq={w.n_heads} Hkv={w.n_kv_heads}")
+    A = mi.attention_inputs(w)
+    got = gpu_attention(M, w, A)
+    sel = np.array([0, 1, 63, 64, 1000, 2047, 2048, 4095], dtype=np.int64)
+    ref = oracle.attention(A["q"], A["k"], A["v"], w.n_heads, w.n_kv_heads, tokens=sel)
+    err = rel_err(got[sel], ref)
+    say(f"  {len(sel)} positions: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL
+
+
+def gpu_block(M, w, h0, BW, W):
+    dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16)
+    at = M.AttnDims(w.T, w.d, w.n_heads, w.n_kv_heads, 128, w.rope_base, w.eps)
+    ws = torch.empty(M.moe_block_workspace_bytes(dm, at), dtype=torch.uint8, device="cuda")
+    h = dev(h0)
+    M.moe_block_forward(dm, at, h, dev(BW["w_qkv"]), dev(BW["w_o"]), dev(W["w_gate"]), dev(W["w1"]), dev(W["w3"]),
+                        dev(W["w2"]), ws)
+    torch.cuda.synchronize()
+    return host(h).astype(np.float64)
+
+
+def check_block(M, w, tokens=None):
+    h0 = mi.residual0(w)
+    BW = mi.block_weights(w)
+    W = mi.layer_weights(w)
+    got = gpu_block(M, w, h0, BW, W)
+    h64 = h0.astype(np.float64)
+    ref = oracle.block(h64, BW["w_qkv"], BW["w_o"], W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, w.n_heads,
+                       w.n_kv_heads, w.rope_base, w.eps, tokens=tokens)
+    toks = np.arange(w.T) if tokens is None else tokens
+    keep = gaps(ref["logits"], w.K)[0] > TIE
+    say(f"  {keep.sum()} of {len(toks)} tokens without a routing near-tie")
+    assert keep.sum() >= 0.9 * len(toks)
+    upd_ref = ref["h2"][keep] - h64[toks][keep]
+    err = np.abs(got[toks][keep] - ref["h2"][keep]).max() / np.abs(upd_ref).max()
+    err_att = np.abs(got[toks][keep] - ref["h2"][keep]).max()
+    say(f"  block update max|d|/max|ref| = {err:.3e} (max|d| = {err_att:.3e})")
+    assert err <= TOL
+
+
+def test_block_small(M):
+    w = mi.Workload("block_small", T=200, d=512, F=512, E=8, K=2, n_heads=4, n_kv_heads=1, seed=941)
+    say(f"[block] small T={w.T} d={w.d} F={w.F} heads {w.n_heads}/{w.n_kv_heads}")
+    check_block(M, w)
+
+
+def test_block_small_tiled(M):
+    # enough rows for the LDS-tiled products (projections and experts)
+    w = mi.Workload("block_tiled", T=1100, d=512, F=512, E=4, K=2, n_heads=8, n_kv_heads=2, seed=942)
+    say(f"[block] tiled T={w.T} d={w.d} F={w.F} E={w.E} heads {w.n_heads}/{w.n_kv_heads}")
+    check_block(M, w, tokens=np.array([0, 1, 500, 1023, 1024, 1099], dtype=np.int64))
+
+
+def test_block_mixtral_width_sampled(M):
+    """Mixtral's attention width (d = 4096, 32/8 heads) over 1024 positions, sampled tokens."""
+    w = mi.Workload("block_wide", T=1024, d=4096, F=1024, E=8, K=2, seed=943)
+    say(f"[block] wide T={w.T} d={w.d} F={w.F} heads {w.n_heads}/{w.n_kv_heads}")
+    check_block(M, w, tokens=np.array([0, 5, 511, 512, 1023], dtype=np.int64))
