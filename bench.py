@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--probe", choices=["copy"], help="plain copy of known size (counter calibration)")
-    p.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
-                   help="time moe_forward (default) or moe_backward (gradients of the layer)")
+    p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "block"], default="forward",
+                   help="time moe_forward (default), moe_backward (gradients of the layer) or moe_block_forward "
+                        "(decoder block: attention and the layer; workloads block_T*)")
     return p.parse_args()
 
 
@@ -108,6 +109,9 @@ def main():
     w = mi.WORKLOADS[args.workload]
     if args.pass_ == "backward":
         backward_bench(args, w)
+        return
+    if args.pass_ == "block":
+        block_bench(args, w)
         return
     dt = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -352,6 +356,135 @@ def backward_bench(args, w):
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"dx and logit gradients of {len(sample)} tokens x {reps} repetitions "
                                          f"({el:.1f}s; the weight-gradient sums are not included)"}
+    print(json.dumps(out), flush=True)
+
+
+BLOCK_METRIC = "Decoder-block tokens/s (causal GQA attention 32/8 heads + MoE layer, d=4096) + TFLOP/s vs peak"
+
+
+def block_bench(args, w):
+    """One step = one moe_block_forward call over a single sequence of w.T positions (norm, q/k/v
+    projection, rotary embedding, causal grouped-query attention, output projection, residual, norm,
+    the mixture-of-experts layer, residual), inputs resident in HBM. The residual stream is updated in
+    place from step to step (its values do not change the work)."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_33_amd as moe
+    from sparse_mixture_experts_33_amd.moe import MOE_BLOCK_NUM_STAGES, MOE_STAGE_ATTENTION, MOE_STAGE_EXPERT_UP
+
+    assert w.dtype == "bf16" and w.layers == 1, "the block is timed on one bf16 layer"
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    t_gen = time.time()
+    dims = moe.Dims(w.T, w.d, w.F, w.E, w.K, moe.MOE_BF16, moe.MOE_LAYOUT_PACKED)
+    at = moe.AttnDims(w.T, w.d, w.n_heads, w.n_kv_heads, w.head_dim, w.rope_base, w.eps)
+    W = mi.layer_weights(w)
+    BW = mi.block_weights(w)
+    L = {k: (dev(v) if v is not None else None) for k, v in W.items()}
+    for name, which in (("w1", moe.MOE_W_UP), ("w3", moe.MOE_W_UP), ("w2", moe.MOE_W_DOWN)):
+        packed = torch.empty_like(L[name])  # load-time weight rearrangement, not timed
+        moe.moe_pack_weights(dims, which, L[name], packed)
+        L[name] = packed
+    wqkv, wo = dev(BW["w_qkv"]), dev(BW["w_o"])
+    h0_host = mi.residual0(w)
+    h = dev(h0_host)
+    ws = torch.empty(moe.moe_block_workspace_bytes(dims, at), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs generated and resident in HBM in {time.time() - t_gen:.1f}s")
+
+    # per timed step: the whole call, the attention kernel and the grouped GEMM 1 (from their dispatches)
+    ev = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for x in e:
+            x.record(stream)  # torch creates the underlying event on its first record
+        ev.append(e)
+    torch.cuda.synchronize()
+    arrays = [moe.stage_event_array({2 * MOE_STAGE_ATTENTION: e[2].cuda_event, 2 * MOE_STAGE_ATTENTION + 1: e[3].cuda_event,
+                                     2 * MOE_STAGE_EXPERT_UP: e[4].cuda_event, 2 * MOE_STAGE_EXPERT_UP + 1: e[5].cuda_event},
+                                    MOE_BLOCK_NUM_STAGES) for e in ev]
+
+    def step(arr=None):
+        moe.moe_block_forward(dims, at, h, wqkv, wo, L["w_gate"], L["w1"], L["w3"], L["w2"], ws,
+                              gate_bias=L["bias"], stage_events=arr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e, arr in zip(ev, arrays):
+        e[0].record(stream)
+        step(arr)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    up_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in ev]))
+
+    # algorithmic work: projections, causal attention (each position attends to itself and the
+    # positions before it: 2 T (T+1) D multiply-adds per query head for q.k and p.v), the layer
+    T, d, D, Hq, Hkv = w.T, w.d, w.head_dim, w.n_heads, w.n_kv_heads
+    att_flops = 2 * Hq * D * T * (T + 1)
+    proj_flops = 2 * T * d * (Hq + 2 * Hkv) * D + 2 * T * Hq * D * d
+    moe_flops = 2 * T * d * w.E + 6 * T * w.K * d * w.F
+    block_flops = att_flops + proj_flops + moe_flops
+    up_flops = 4 * T * w.K * d * w.F
+    att_tf = att_flops / (att_ms * 1e-3) / 1e12
+    out = {
+        "metric": BLOCK_METRIC,
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) residual stream, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "pass": "block", "T": T, "d": d, "F": w.F, "E": w.E, "K": w.K,
+                   "n_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "rope_base": w.rope_base,
+                   "weight_layout": "fragment-packed experts, row-major attention weights",
+                   "parallelism": "single GPU"},
+        "step_tflops": round(block_flops / (call_ms * 1e-3) / 1e12, 2),
+        "step_frac_mfma": round(block_flops / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "block_ms": round(call_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(att_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attention (causal grouped-query flash attention)", "kernel_ms": round(att_ms, 4),
+                     "algorithmic": {"flops": att_flops}},
+        "expert_up": {"achieved": round(up_flops / (up_ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                      "kernel_ms": round(up_ms, 4), "flops": up_flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        # early positions: the oracle projects keys and values of every position up to the last one
+        sample = np.array([0, 85, 170, 255], dtype=np.int64)
+        h64 = h0_host.astype(np.float64)
+        done, reps, t1 = 0, 0, time.perf_counter()
+        while True:
+            oracle.block(h64, BW["w_qkv"], BW["w_o"], W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, Hq, Hkv,
+                         w.rope_base, w.eps, tokens=sample, bias=W["bias"], threads=threads)
+            done += len(sample)
+            reps += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"block outputs of positions {list(map(int, sample))} (keys and values of "
+                                         f"positions 0-255 projected each time) x {reps} repetitions ({el:.1f}s)"}
     print(json.dumps(out), flush=True)
 
 

@@ -103,7 +103,9 @@ enum {
   MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1) */
   MOE_STAGE_EXPERT_DOWN = 3, /* hidden x w2 (grouped GEMM 2) */
   MOE_STAGE_COMBINE = 4,     /* gate-weighted sum back to token order */
-  MOE_NUM_STAGES = 5
+  MOE_NUM_STAGES = 5,
+  MOE_STAGE_ATTENTION = 5,   /* moe_block_forward only: the attention kernel */
+  MOE_BLOCK_NUM_STAGES = 6   /* moe_block_forward's stage_events array holds 2 * MOE_BLOCK_NUM_STAGES entries */
 };
 
 /* Router (csdn explainer sections 2.1-2.3; xyznot.com "Método").
@@ -251,9 +253,11 @@ moe_status moe_attention(const moe_attn_dims* attn, const void* q, const void* k
  *   w_qkv [(n_heads + 2 n_kv_heads) * D][d] bf16, row-major (rows: the q heads, then k, then v)
  *   w_o   [d][n_heads * D] bf16, row-major
  *   w_gate, w1, w3, w2: the layer's weights as for moe_forward (dims->dtype must be MOE_BF16)
- *   moe->T and moe->d must equal attn->T and attn->d. opts: gate_bias and stage_events as for
- *   moe_forward (the events time the mixture-of-experts stages); y_dtype and accumulate are
- *   ignored (the layer's output is added to h).
+ *   moe->T and moe->d must equal attn->T and attn->d. opts: gate_bias as for moe_forward;
+ *   stage_events, if not NULL, an array of 2 * MOE_BLOCK_NUM_STAGES events: entries 0 .. 2 *
+ *   MOE_NUM_STAGES - 1 time the layer's stages as in moe_forward, entries 2 * MOE_STAGE_ATTENTION
+ *   and 2 * MOE_STAGE_ATTENTION + 1 the attention kernel; y_dtype and accumulate are ignored
+ *   (the layer's output is added to h).
  *   workspace: >= moe_block_workspace_bytes() bytes of device memory, 256-byte aligned.
  * Supported: bf16, head_dim 128, n_heads a multiple of 4 * n_kv_heads, d a multiple of 256
  * (with the layer's limits). */

@@ -543,7 +543,12 @@ moe_status moe_block_forward(const moe_dims* dims, const moe_attn_dims* attn, co
   moe::launch_rmsnorm(h, at.T, at.d, at.eps, at_(L.u), s);
   moe::launch_expert_down(MOE_BF16, rm, at_(L.u), off, at.T, (Hq + 2 * Hkv) * D, at.d, 1, w_qkv, qkv, 1, nullptr, s);
   moe::launch_rope_qkv(qkv, at.T, Hq, Hkv, (double)at.rope_base, at_(L.q), at_(L.k), at_(L.v), s);
+  void* const* ev = opts ? opts->stage_events : nullptr;
+  if (ev)  // the attention kernel records its own dispatch (see launch_kernel)
+    moe::pending_dispatch_events() = {static_cast<hipEvent_t>(ev[2 * MOE_STAGE_ATTENTION]),
+                                      static_cast<hipEvent_t>(ev[2 * MOE_STAGE_ATTENTION + 1])};
   moe::launch_attention(at_(L.q), at_(L.k), at_(L.v), at_(L.o), at.T, Hq, Hkv, s);
+  moe::pending_dispatch_events() = moe::DispatchEvents{};
   moe::launch_expert_down(MOE_BF16, rm, at_(L.o), off, at.T, at.d, Hq * D, 1, w_o, a, 1, nullptr, s);
   moe::launch_residual_norm(h, a, at.T, at.d, at.eps, at_(L.x2), s);
   MOE_TRY(check_launch("moe_block_forward (attention)"));

@@ -19,6 +19,7 @@ MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
 MOE_W_UP, MOE_W_DOWN = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_COMBINE = range(5)
 MOE_NUM_STAGES = 5
+MOE_STAGE_ATTENTION, MOE_BLOCK_NUM_STAGES = 5, 6  # moe_block_forward's extra stage and array size
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 
 # every symbol include/moe.h declares
@@ -146,13 +147,14 @@ def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16, stage_
                     stage_events)
 
 
-def stage_event_array(events: dict):
-    """ctypes array of 2*MOE_NUM_STAGES hipEvent_t handles for moe_opts.stage_events.
+def stage_event_array(events: dict, stages: int = MOE_NUM_STAGES):
+    """ctypes array of 2*stages hipEvent_t handles for moe_opts.stage_events (stages:
+    MOE_NUM_STAGES for moe_forward, MOE_BLOCK_NUM_STAGES for moe_block_forward).
 
     events maps an array position (2*stage for the start, 2*stage+1 for the end of that stage's
     kernel) to a raw hipEvent_t handle (e.g. torch.cuda.Event(...).cuda_event); other positions
     stay NULL."""
-    arr = (ctypes.c_void_p * (2 * MOE_NUM_STAGES))()
+    arr = (ctypes.c_void_p * (2 * stages))()
     for i, h in events.items():
         arr[i] = h
     return arr
