@@ -6,7 +6,7 @@
 //
 // Attention (flash form, one pass over the keys with a running softmax): a workgroup takes 64
 // query positions of the 4 query heads that share one key-value head (group size Hq/Hkv a
-// multiple of 4), one wavefront per head, so every 64-key tile staged in LDS serves 4 heads.
+// multiple of 4), two wavefronts per head, so every 64-key tile staged in LDS serves 4 heads.
 // Per wavefront and key tile, on 16x16x32 bf16 MFMAs with fp32 sums:
 //   S^T = K Q^T       (K from LDS, the wavefront's Q fragments held in registers all along)
 //   running max / sum per query, P = exp(S - max) rounded to bf16
@@ -64,11 +64,26 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
 
 __device__ inline float max4(f32x4_t v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
 
+// Two fp32 values to a bf16 pair (round to nearest even) with the hardware conversion.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// The running maximum of a query moves only when a tile's maximum exceeds it by more than this
+// (in units of log2 after scaling): the exponentials then stay below 2^8, and the rescaling of the
+// output accumulators, which every lane of the wavefront skips together, is rare after the first tiles.
+constexpr float kLazyMax = 8.0f;
+
 // q [Hq][T][128], k, v [Hkv][T][128] bf16 -> o [T][Hq*128] bf16. Grid: (T/64 rounded up) * (Hq/4)
-// workgroups of 4 wavefronts.
-__global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+// workgroups of 8 wavefronts: wavefront w takes query head 4 (group) + w/2 and the query positions
+// q0 + 32 (w%2) .. +31 (two 16-position blocks), so two wavefronts share each SIMD and one's softmax
+// runs under the other's MFMAs.
+__global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                            const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
                                                            int64_t T, int Hq, int Hkv, float scale_log2) {
+  constexpr int QJ = 2;  // 16-position query blocks per wavefront
   __shared__ __attribute__((aligned(16))) bf16_t ks[2][kKB * kKRow];
   __shared__ __attribute__((aligned(16))) bf16_t vs[2][kKB * kVRow];
 
@@ -76,50 +91,51 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nqb = (int)((T + kQB - 1) / kQB), nhg = Hq / 4;
   const int qb = nqb - 1 - (int)(blockIdx.x / nhg);  // longest blocks first
-  const int hq = (int)(blockIdx.x % nhg) * 4 + wave;
-  const int hk = (hq / (Hq / Hkv));  // the 4 heads of a workgroup share it (group size % 4 == 0)
+  const int hq = (int)(blockIdx.x % nhg) * 4 + (wave >> 1);
+  const int hk = hq / (Hq / Hkv);  // the 4 heads of a workgroup share it (group size % 4 == 0)
   const int64_t q0 = (int64_t)qb * kQB;
+  const int qw = 32 * (wave & 1);  // first query of this wavefront within the block
 
   // Q fragments as the B operand of S^T = K Q^T: query block j, k-chunk c (32 dims); lane: query
-  // q0 + 16 j + li, dims 32 c + 8 g .. +7. Rows past T load the last row (never stored).
-  u32x4_t qf[4][4];
+  // q0 + qw + 16 j + li, dims 32 c + 8 g .. +7. Rows past T load the last row (never stored).
+  u32x4_t qf[QJ][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t t = min(q0 + 16 * j + li, T - 1);
+  for (int j = 0; j < QJ; ++j) {
+    const int64_t t = min(q0 + qw + 16 * j + li, T - 1);
     const bf16_t* row = q + ((int64_t)hq * T + t) * kHD;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qf[j][c] = load16(row + 32 * c + 8 * g);
   }
 
-  // K/V tile loads: 64 rows x 256 B each, 16 B per thread per round, 4 rounds per tile
+  // K/V tile loads: 64 rows x 256 B each, 16 B per thread per round, 2 rounds per tile
   const bf16_t* kbase = k + (int64_t)hk * T * kHD;
   const bf16_t* vbase = v + (int64_t)hk * T * kHD;
-  const int lr = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 8;  // row (of 16) and column of this thread
-  u32x4_t kreg[4], vreg[4];
+  const int lr = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 8;  // row (of 32) and column of this thread
+  u32x4_t kreg[2], vreg[2];
   auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t key = min(k0 + lr + 16 * r, T - 1);  // keys past T are masked below
+    for (int r = 0; r < 2; ++r) {
+      const int64_t key = min(k0 + lr + 32 * r, T - 1);  // keys past T are masked below
       kreg[r] = load16(kbase + key * kHD + lc);
       vreg[r] = load16(vbase + key * kHD + lc);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      store16(&ks[buf][(lr + 16 * r) * kKRow + lc], kreg[r]);
-      store16(&vs[buf][(lr + 16 * r) * kVRow + lc], vreg[r]);
+    for (int r = 0; r < 2; ++r) {
+      store16(&ks[buf][(lr + 32 * r) * kKRow + lc], kreg[r]);
+      store16(&vs[buf][(lr + 32 * r) * kVRow + lc], vreg[r]);
     }
   };
 
-  f32x4_t oacc[8][4];  // O^T: dim block db (16 dims) x query block j
+  f32x4_t oacc[8][QJ];  // O^T: dim block d (16 dims) x query block j
 #pragma unroll
   for (int d = 0; d < 8; ++d)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) oacc[d][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[4], lrun[4];  // running max (all four lanes of a query agree) and this lane's partial sum
+    for (int j = 0; j < QJ; ++j) oacc[d][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[QJ], lrun[QJ];  // running max (all four lanes of a query agree) and this lane's partial sum
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < QJ; ++j) {
     mrun[j] = -INFINITY;
     lrun[j] = 0.f;
   }
@@ -134,11 +150,11 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restr
     if (st + 1 < nsteps) gload(k0 + kKB);
 
     // S^T = K Q^T: key block i (A operand rows = keys, from LDS), query block j
-    f32x4_t s[4][4];
+    f32x4_t s[4][QJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < QJ; ++j) s[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4_t kf[4];
@@ -147,33 +163,47 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restr
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[i][j] = mfma_bf16(kf[i], qf[j][c], s[i][j]);
+        for (int j = 0; j < QJ; ++j) s[i][j] = mfma_bf16(kf[i], qf[j][c], s[i][j]);
     }
     // causal mask on the diagonal tile (k0 == q0), which also holds every key past T
     if (st == nsteps - 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < QJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int kk = 16 * i + 4 * g + r, qq = 16 * j + li;
+            const int kk = 16 * i + 4 * g + r, qq = qw + 16 * j + li;
             if (kk > qq || k0 + kk >= T) s[i][j][r] = -INFINITY;
           }
     }
     // running softmax per query column; P^T as the B operand of the second product: key chunk kc
     // (32 keys = key blocks 2kc, 2kc+1), lane slots 0-3 = keys 4g..4g+3 of block 2kc, slots 4-7 the
     // same of block 2kc+1
-    u32x4_t pf[2][4];
+    u32x4_t pf[2][QJ];
+    float mx[QJ];
+    bool grow = false;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(mrun[j], mx);
-      const float alpha = exp2f((mrun[j] - mnew) * scale_log2);
-      mrun[j] = mnew;
-      const float mb = mnew * scale_log2;
+    for (int j = 0; j < QJ; ++j) {
+      float m = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
+      m = fmaxf(m, __shfl_xor(m, 16, kWave));
+      mx[j] = fmaxf(m, __shfl_xor(m, 32, kWave));
+      grow |= (mx[j] - mrun[j]) * scale_log2 > kLazyMax;  // also true on the first tile (mrun = -inf)
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int j = 0; j < QJ; ++j) {
+        const float mnew = fmaxf(mrun[j], mx[j]);
+        const float alpha = exp2f((mrun[j] - mnew) * scale_log2);
+        mrun[j] = mnew;
+        lrun[j] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QJ; ++j) {
+      const float mb = mrun[j] * scale_log2;
       float p[4][4], sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -182,18 +212,16 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restr
           p[i][r] = exp2f(fmaf(s[i][j][r], scale_log2, -mb));
           sum += p[i][r];
         }
-      lrun[j] = lrun[j] * alpha + sum;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
+      lrun[j] += sum;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
-        pf[kc][j] = u32x4_t{pack_bf16x2(p[2 * kc][0], p[2 * kc][1]), pack_bf16x2(p[2 * kc][2], p[2 * kc][3]),
-                            pack_bf16x2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
-                            pack_bf16x2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
+        pf[kc][j] = u32x4_t{cvt_bf16x2(p[2 * kc][0], p[2 * kc][1]), cvt_bf16x2(p[2 * kc][2], p[2 * kc][3]),
+                            cvt_bf16x2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
+                            cvt_bf16x2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
     }
     // O^T += V^T P^T: A operand (dims x keys) by transposing reads of the V tile: in each group of
     // 16 lanes, lanes 4a..4a+3 address row a's 16 columns and lane i receives column i of the 4
-    // rows, so lane (g, i) gets dim 16 db + i at keys 4g..4g+3 of key blocks 2kc and 2kc+1
+    // rows, so lane (g, i) gets dim 16 d + i at keys 4g..4g+3 of key blocks 2kc and 2kc+1
     typedef __attribute__((ext_vector_type(4))) short v4s;
     typedef __attribute__((address_space(3))) v4s* lds_v4s;
     const int ta = (lane >> 2) & 3, tc = lane & 3;
@@ -207,28 +235,28 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(const bf16_t* __restr
         const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
         const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[d][j] = mfma_bf16(vf, pf[kc][j], oacc[d][j]);
+        for (int j = 0; j < QJ; ++j) oacc[d][j] = mfma_bf16(vf, pf[kc][j], oacc[d][j]);
       }
     // the other buffer was last read in the previous step, before the barrier that ended it
     if (st + 1 < nsteps) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // O = O^T / sum, rounded to bf16; lane: query q0 + 16 j + li, dims 16 db + 4 g .. +3
+  // O = O^T / sum, rounded to bf16; lane: query q0 + qw + 16 j + li, dims 16 d + 4 g .. +3
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < QJ; ++j) {
     float l = lrun[j];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     const float inv = 1.0f / l;
-    const int64_t t = q0 + 16 * j + li;
+    const int64_t t = q0 + qw + 16 * j + li;
     if (t >= T) continue;
     bf16_t* dst = o + t * (int64_t)Hq * kHD + (int64_t)hq * kHD + 4 * g;
 #pragma unroll
     for (int d = 0; d < 8; ++d)
       *reinterpret_cast<u32x2_t*>(dst + 16 * d) =
-          u32x2_t{pack_bf16x2(oacc[d][j][0] * inv, oacc[d][j][1] * inv),
-                  pack_bf16x2(oacc[d][j][2] * inv, oacc[d][j][3] * inv)};
+          u32x2_t{cvt_bf16x2(oacc[d][j][0] * inv, oacc[d][j][1] * inv),
+                  cvt_bf16x2(oacc[d][j][2] * inv, oacc[d][j][3] * inv)};
   }
 }
 
@@ -279,7 +307,7 @@ void launch_attention(const void* q, const void* k, const void* v, void* o, int6
                       hipStream_t s) {
   const int64_t nqb = (T + kQB - 1) / kQB;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHD));
-  launch_kernel(attention_kernel, dim3((unsigned)(nqb * (Hq / 4))), dim3(256), 0, s, static_cast<const bf16_t*>(q),
+  launch_kernel(attention_kernel, dim3((unsigned)(nqb * (Hq / 4))), dim3(512), 0, s, static_cast<const bf16_t*>(q),
                 static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), static_cast<bf16_t*>(o), T, Hq, Hkv,
                 scale_log2);
 }
