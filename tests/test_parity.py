@@ -41,6 +41,9 @@ SMALL = {
     "e16_k4_bf16": mi.Workload("e16_k4_bf16", T=130, d=128, F=192, E=16, K=4, dtype="bf16", seed=615),
     "e1_k1_f32": mi.Workload("e1_k1_f32", T=70, d=128, F=128, E=1, K=1, dtype="f32", seed=616),
     "e64_k8_f32": mi.Workload("e64_k8_f32", T=40, d=64, F=64, E=64, K=8, dtype="f32", seed=617),
+    # few bf16 tokens (the per-token router, a single-wavefront permutation)
+    "few_t17_bf16": mi.Workload("few_t17_bf16", T=17, d=256, F=256, dtype="bf16", seed=618),
+    "few_t64_e16_k8_bf16": mi.Workload("few_t64_e16_k8_bf16", T=64, d=192, F=192, E=16, K=8, dtype="bf16", seed=619),
 }
 
 
@@ -409,6 +412,8 @@ FUSED = {
     "fused_k4_e16": mi.Workload("fused_k4_e16", T=100, d=128, F=256, E=16, K=4, dtype="bf16", seed=633),
     "fused_f32_k8": mi.Workload("fused_f32_k8", T=40, d=64, F=64, E=64, K=8, dtype="f32", seed=634),
     "fused_decode": mi.Workload("fused_decode", T=32, d=4096, F=14336, dtype="bf16", seed=202),
+    "fused_t1": mi.Workload("fused_t1", T=1, d=256, F=256, dtype="bf16", seed=635),
+    "fused_t64_e16_k8": mi.Workload("fused_t64_e16_k8", T=64, d=192, F=192, E=16, K=8, dtype="bf16", seed=636),
 }
 
 

@@ -14,6 +14,8 @@ CASES = {
     "stream_bf16": mi.Workload("stream_bf16", T=300, d=256, F=512, dtype="bf16", seed=621),
     # LDS-tiled expert GEMMs with a split down projection
     "tiled_bf16": mi.Workload("tiled_bf16", T=700, d=256, F=2048, E=4, K=2, dtype="bf16", seed=622),
+    # few tokens: the per-token router and the single-wavefront permutation
+    "few_bf16": mi.Workload("few_bf16", T=32, d=256, F=512, dtype="bf16", seed=623),
 }
 
 
