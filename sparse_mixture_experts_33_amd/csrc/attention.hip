@@ -71,6 +71,11 @@ __device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// 2^x with the hardware instruction alone. exp2f wraps it in a rescaling that keeps subnormal
+// results; here a result below 2^-126 comes out as zero instead, i.e. a key whose weight is under
+// 2^-126 of the running maximum's drops out of the sums, far below the bf16 rounding of the weights.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // The running maximum of a query moves only when a tile's maximum exceeds it by more than this
 // (in units of log2 after scaling): the exponentials then stay below 2^8, and the rescaling of the
 // output accumulators, which every lane of the wavefront skips together, is rare after the first tiles.
@@ -136,13 +141,21 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
   float mrun[QJ], lrun[QJ];  // running max (all four lanes of a query agree) and this lane's partial sum
 #pragma unroll
   for (int j = 0; j < QJ; ++j) {
-    mrun[j] = -INFINITY;
+    mrun[j] = -1e30f;  // finite, so that the first tile's exponents are huge rather than NaN
     lrun[j] = 0.f;
   }
 
   const int nsteps = qb + 1;  // key tiles 0..qb; the last one is the diagonal tile
   gload(0);
   lstore(0);
+  // The Q fragments must have landed before the loop. Left alone, the compiler sinks their loads
+  // to the loop entry; the wait for them, merged over the back edge, then counts the next tile's
+  // K/V prefetch too and stalls every step's first product on it. An empty asm that reads them
+  // pins the loads here and makes the wait happen once.
+#pragma unroll
+  for (int j = 0; j < QJ; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qf[j][c]));
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
@@ -177,39 +190,56 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
             if (kk > qq || k0 + kk >= T) s[i][j][r] = -INFINITY;
           }
     }
-    // running softmax per query column; P^T as the B operand of the second product: key chunk kc
-    // (32 keys = key blocks 2kc, 2kc+1), lane slots 0-3 = keys 4g..4g+3 of block 2kc, slots 4-7 the
-    // same of block 2kc+1
-    u32x4_t pf[2][QJ];
-    float mx[QJ];
+    // running softmax per query column. The exponents t = (S - running max) * scale_log2 are formed
+    // first and their maximum decides whether the running max must move: being results of
+    // arithmetic, they take the max instructions without the NaN-quieting each raw MFMA output
+    // would need. P^T as the B operand of the second product: key chunk kc (32 keys = key blocks 2kc,
+    // 2kc+1), lane slots 0-3 = keys 4g..4g+3 of block 2kc, slots 4-7 the same of block 2kc+1
+    float t[QJ][4][4];
     bool grow = false;
 #pragma unroll
     for (int j = 0; j < QJ; ++j) {
-      float m = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
+      const float mb = mrun[j] * scale_log2;
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          t[j][i][r] = fmaf(s[i][j][r], scale_log2, -mb);
+          m = fmaxf(m, t[j][i][r]);
+        }
       m = fmaxf(m, __shfl_xor(m, 16, kWave));
-      mx[j] = fmaxf(m, __shfl_xor(m, 32, kWave));
-      grow |= (mx[j] - mrun[j]) * scale_log2 > kLazyMax;  // also true on the first tile (mrun = -inf)
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      grow |= m > kLazyMax;  // also true on the first tile (mrun starts far below any score)
     }
     if (__any(grow)) {
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
-        const float mnew = fmaxf(mrun[j], mx[j]);
-        const float alpha = exp2f((mrun[j] - mnew) * scale_log2);
+        float m = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float mnew = fmaxf(mrun[j], m);
+        const float alpha = exp2_hw((mrun[j] - mnew) * scale_log2);
         mrun[j] = mnew;
         lrun[j] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
+        const float mb = mnew * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[j][i][r] = fmaf(s[i][j][r], scale_log2, -mb);
       }
     }
+    u32x4_t pf[2][QJ];
 #pragma unroll
     for (int j = 0; j < QJ; ++j) {
-      const float mb = mrun[j] * scale_log2;
       float p[4][4], sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[i][r] = exp2f(fmaf(s[i][j][r], scale_log2, -mb));
+          p[i][r] = exp2_hw(t[j][i][r]);
           sum += p[i][r];
         }
       lrun[j] += sum;
