@@ -27,8 +27,12 @@ namespace {
 constexpr int kHD = 128;         // head width
 constexpr int kQB = 64;          // query positions per workgroup (per wavefront)
 constexpr int kKB = 64;          // keys per tile
-constexpr int kKRow = kHD + 8;   // LDS row of the K tile (elements): 272 B, conflict-free 16 B reads
-constexpr int kVRow = kHD + 16;  // LDS row of the V tile: 288 B, conflict-free transposing reads
+// LDS rows of the K and V tiles (elements): 288 B. Measured on gfx950 with the bank-conflict
+// counter, this stride leaves both the 16-byte K-fragment reads and the transposing V reads free
+// of conflicts; 272 B, conflict-free for the K reads under a plain 32-bank model, doubles their
+// LDS cycles.
+constexpr int kKRow = kHD + 16;
+constexpr int kVRow = kHD + 16;
 
 // qkv [T][(Hq + 2 Hkv) * 128] fp32 -> q [Hq][T][128], k [Hkv][T][128], v [Hkv][T][128] bf16, with the
 // rotary embedding on q and k: in each head the pair (i, i + 64) of position t turns by the angle
@@ -83,23 +87,33 @@ constexpr float kLazyMax = 8.0f;
 
 // q [Hq][T][128], k, v [Hkv][T][128] bf16 -> o [T][Hq*128] bf16. Grid: (T/64 rounded up) * (Hq/4)
 // workgroups of 8 wavefronts: wavefront w takes query head 4 (group) + w/2 and the query positions
-// q0 + 32 (w%2) .. +31 (two 16-position blocks), so two wavefronts share each SIMD and one's softmax
-// runs under the other's MFMAs.
+// q0 + 32 (w%2) .. +31 (two 16-position blocks).
+//
+// Two phases. Wavefronts w and w + 4 share a SIMD; those below 4 (phase 0) run each key tile
+// straight through (scores, softmax, second product), those from 4 up (phase 1) run half a tile
+// behind: between two barriers they finish the previous tile (exponentials, second product) and
+// start this one (scores, the running-max check). So while one wavefront of a SIMD is in its
+// softmax, the other issues MFMAs. Each phase stages its half of the next tile's rows, at its own
+// point between barriers; three LDS buffers keep a tile resident until the later phase is done
+// with it (tile n+1 is written while phase 1 may still read tile n-1).
 __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                            const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
                                                            int64_t T, int Hq, int Hkv, float scale_log2) {
   constexpr int QJ = 2;  // 16-position query blocks per wavefront
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][kKB * kKRow];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[2][kKB * kVRow];
+  constexpr int NB = 3;  // LDS tile buffers
+  __shared__ __attribute__((aligned(16))) bf16_t ks[NB][kKB * kKRow];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[NB][kKB * kVRow];
 
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int phase = wave >> 2;
   const int nqb = (int)((T + kQB - 1) / kQB), nhg = Hq / 4;
   const int qb = nqb - 1 - (int)(blockIdx.x / nhg);  // longest blocks first
   const int hq = (int)(blockIdx.x % nhg) * 4 + (wave >> 1);
   const int hk = hq / (Hq / Hkv);  // the 4 heads of a workgroup share it (group size % 4 == 0)
   const int64_t q0 = (int64_t)qb * kQB;
   const int qw = 32 * (wave & 1);  // first query of this wavefront within the block
+  const int nsteps = qb + 1;       // key tiles 0..qb; the last one is the diagonal tile
 
   // Q fragments as the B operand of S^T = K Q^T: query block j, k-chunk c (32 dims); lane: query
   // q0 + qw + 16 j + li, dims 32 c + 8 g .. +7. Rows past T load the last row (never stored).
@@ -112,15 +126,16 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
     for (int c = 0; c < 4; ++c) qf[j][c] = load16(row + 32 * c + 8 * g);
   }
 
-  // K/V tile loads: 64 rows x 256 B each, 16 B per thread per round, 2 rounds per tile
+  // K/V tile rows: a phase stages rows 32 phase .. +31 of a tile (16 B per thread per row block)
   const bf16_t* kbase = k + (int64_t)hk * T * kHD;
   const bf16_t* vbase = v + (int64_t)hk * T * kHD;
-  const int lr = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 8;  // row (of 32) and column of this thread
+  const int tid = (wave & 3) * kWave + lane;  // thread index within the phase
+  const int lr = 32 * phase + (tid >> 4), lc = (tid & 15) * 8;  // first row and column of this thread
   u32x4_t kreg[2], vreg[2];
-  auto gload = [&](int64_t k0) {
+  auto gload = [&](int tile) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int64_t key = min(k0 + lr + 32 * r, T - 1);  // keys past T are masked below
+      const int64_t key = min((int64_t)tile * kKB + lr + 16 * r, T - 1);  // keys past T are masked
       kreg[r] = load16(kbase + key * kHD + lc);
       vreg[r] = load16(vbase + key * kHD + lc);
     }
@@ -128,9 +143,15 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      store16(&ks[buf][(lr + 32 * r) * kKRow + lc], kreg[r]);
-      store16(&vs[buf][(lr + 32 * r) * kVRow + lc], vreg[r]);
+      store16(&ks[buf][(lr + 16 * r) * kKRow + lc], kreg[r]);
+      store16(&vs[buf][(lr + 16 * r) * kVRow + lc], vreg[r]);
     }
+  };
+  // LDS-only barrier: the global loads in flight (the next tiles) are not waited for
+  auto barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
   f32x4_t oacc[8][QJ];  // O^T: dim block d (16 dims) x query block j
@@ -138,30 +159,22 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
   for (int d = 0; d < 8; ++d)
 #pragma unroll
     for (int j = 0; j < QJ; ++j) oacc[d][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[QJ], lrun[QJ];  // running max (all four lanes of a query agree) and this lane's partial sum
+  // running max per query in exponent units (max * scale_log2; all four lanes of a query agree) and
+  // this lane's partial sum of the weights
+  float mrun[QJ], lrun[QJ];
 #pragma unroll
   for (int j = 0; j < QJ; ++j) {
-    mrun[j] = -1e30f;  // finite, so that the first tile's exponents are huge rather than NaN
+    mrun[j] = 0.f;
     lrun[j] = 0.f;
   }
 
-  const int nsteps = qb + 1;  // key tiles 0..qb; the last one is the diagonal tile
-  gload(0);
-  lstore(0);
-  // The Q fragments must have landed before the loop. Left alone, the compiler sinks their loads
-  // to the loop entry; the wait for them, merged over the back edge, then counts the next tile's
-  // K/V prefetch too and stalls every step's first product on it. An empty asm that reads them
-  // pins the loads here and makes the wait happen once.
-#pragma unroll
-  for (int j = 0; j < QJ; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qf[j][c]));
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    const int64_t k0 = (int64_t)st * kKB;
-    if (st + 1 < nsteps) gload(k0 + kKB);
-
+  // Scores and the running-max step of tile st (in LDS buffer buf): t = exponents of the weights,
+  // t = S * scale_log2 - running max. They are formed in place of the scores, and their maximum
+  // decides whether the running max must move: being results of arithmetic, they take the max
+  // instructions without the NaN-quieting each raw MFMA output would need. The first tile always
+  // sets the running max (to its own maximum).
+  float t[QJ][4][4];
+  auto scores = [&](int st, int buf) {
     // S^T = K Q^T: key block i (A operand rows = keys, from LDS), query block j
     f32x4_t s[4][QJ];
 #pragma unroll
@@ -180,6 +193,7 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
     }
     // causal mask on the diagonal tile (k0 == q0), which also holds every key past T
     if (st == nsteps - 1) {
+      const int64_t k0 = (int64_t)st * kKB;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -190,47 +204,47 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
             if (kk > qq || k0 + kk >= T) s[i][j][r] = -INFINITY;
           }
     }
-    // running softmax per query column. The exponents t = (S - running max) * scale_log2 are formed
-    // first and their maximum decides whether the running max must move: being results of
-    // arithmetic, they take the max instructions without the NaN-quieting each raw MFMA output
-    // would need. P^T as the B operand of the second product: key chunk kc (32 keys = key blocks 2kc,
-    // 2kc+1), lane slots 0-3 = keys 4g..4g+3 of block 2kc, slots 4-7 the same of block 2kc+1
-    float t[QJ][4][4];
-    bool grow = false;
+    float m[QJ];
+    bool grow = st == 0;
 #pragma unroll
     for (int j = 0; j < QJ; ++j) {
-      const float mb = mrun[j] * scale_log2;
-      float m = -INFINITY;
+      m[j] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          t[j][i][r] = fmaf(s[i][j][r], scale_log2, -mb);
-          m = fmaxf(m, t[j][i][r]);
+          t[j][i][r] = fmaf(s[i][j][r], scale_log2, -mrun[j]);
+          m[j] = fmaxf(m[j], t[j][i][r]);
         }
-      m = fmaxf(m, __shfl_xor(m, 16, kWave));
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      grow |= m > kLazyMax;  // also true on the first tile (mrun starts far below any score)
+      grow |= m[j] > kLazyMax;
     }
     if (__any(grow)) {
 #pragma unroll
       for (int j = 0; j < QJ; ++j) {
-        float m = fmaxf(fmaxf(max4(s[0][j]), max4(s[1][j])), fmaxf(max4(s[2][j]), max4(s[3][j])));
-        m = fmaxf(m, __shfl_xor(m, 16, kWave));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float mnew = fmaxf(mrun[j], m);
-        const float alpha = exp2_hw((mrun[j] - mnew) * scale_log2);
-        mrun[j] = mnew;
+        float mx = fmaxf(m[j], __shfl_xor(m[j], 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        // the running max moves up by dm (to the tile's max on the first tile)
+        const float dm = st == 0 ? mx : fmaxf(mx, 0.f);
+        const float alpha = st == 0 ? 0.f : exp2_hw(-dm);
+        mrun[j] += dm;
         lrun[j] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
-        const float mb = mnew * scale_log2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) t[j][i][r] = fmaf(s[i][j][r], scale_log2, -mb);
+          for (int r = 0; r < 4; ++r) t[j][i][r] -= dm;
       }
     }
+  };
+
+  // Weights P = 2^t rounded to bf16 and O^T += V^T P^T with the V tile in buffer buf. P^T is the B
+  // operand: key chunk kc (32 keys = key blocks 2kc, 2kc+1), lane slots 0-3 = keys 4g..4g+3 of
+  // block 2kc, slots 4-7 the same of block 2kc+1. The A operand (dims x keys) comes from
+  // transposing reads of the V tile: in each group of 16 lanes, lanes 4a..4a+3 address row a's 16
+  // columns and lane i receives column i of the 4 rows, so lane (g, i) gets dim 16 d + i at keys
+  // 4g..4g+3 of key blocks 2kc and 2kc+1.
+  auto weigh = [&](int buf) {
     u32x4_t pf[2][QJ];
 #pragma unroll
     for (int j = 0; j < QJ; ++j) {
@@ -249,9 +263,6 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
                             cvt_bf16x2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
                             cvt_bf16x2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
     }
-    // O^T += V^T P^T: A operand (dims x keys) by transposing reads of the V tile: in each group of
-    // 16 lanes, lanes 4a..4a+3 address row a's 16 columns and lane i receives column i of the 4
-    // rows, so lane (g, i) gets dim 16 d + i at keys 4g..4g+3 of key blocks 2kc and 2kc+1
     typedef __attribute__((ext_vector_type(4))) short v4s;
     typedef __attribute__((address_space(3))) v4s* lds_v4s;
     const int ta = (lane >> 2) & 3, tc = lane & 3;
@@ -267,9 +278,49 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
 #pragma unroll
         for (int j = 0; j < QJ; ++j) oacc[d][j] = mfma_bf16(vf, pf[kc][j], oacc[d][j]);
       }
-    // the other buffer was last read in the previous step, before the barrier that ended it
-    if (st + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // tile 0 in buffer 0 (both phases' rows)
+  gload(0);
+  lstore(0);
+  // The Q fragments must have landed before the loop. Left alone, the compiler sinks their loads
+  // to the loop entry; the wait for them, merged over the back edge, then counts the next tile's
+  // K/V prefetch too and stalls every step's first product on it. An empty asm that reads them
+  // pins the loads here and makes the wait happen once.
+#pragma unroll
+  for (int j = 0; j < QJ; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qf[j][c]));
+  barrier();
+  // Between barriers st-1 and st, tile st+1 is staged by both phases into buffer (st+1) % 3, whose
+  // previous tile st-2 both phases finished before barrier st-1.
+  if (phase == 0) {
+    int buf = 0;
+    for (int st = 0; st < nsteps; ++st) {
+      const int nbuf = buf == NB - 1 ? 0 : buf + 1;
+      if (st + 1 < nsteps) gload(st + 1);
+      scores(st, buf);
+      weigh(buf);
+      if (st + 1 < nsteps) lstore(nbuf);
+      barrier();
+      buf = nbuf;
+    }
+  } else {
+    if (nsteps > 1) gload(1);
+    int buf = 0, pbuf = NB - 1;
+    for (int st = 0; st < nsteps; ++st) {
+      const int nbuf = buf == NB - 1 ? 0 : buf + 1;
+      if (st > 0) weigh(pbuf);  // tile st-1, staged before barrier st-2
+      if (st + 1 < nsteps) {
+        lstore(nbuf);
+        if (st + 2 < nsteps) gload(st + 2);
+      }
+      scores(st, buf);
+      barrier();
+      pbuf = buf;
+      buf = nbuf;
+    }
+    weigh(pbuf);
   }
 
   // O = O^T / sum, rounded to bf16; lane: query q0 + qw + 16 j + li, dims 16 d + 4 g .. +3
