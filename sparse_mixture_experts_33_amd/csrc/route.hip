@@ -11,6 +11,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -157,6 +159,46 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
     if (lane == tt && t0 + tt < ntok) finalize_token<EMAX>(acc[tt], t0 + tt, E, K, bias, topk_idx, topk_w, logits);
 }
 
+// Many tokens, bf16, E = 8, d <= 4096: W_g (d rows of 16 bytes) is staged in LDS once per
+// workgroup and each wavefront then takes tokens in turn, so W_g is read from L2 once per
+// workgroup rather than once per token. Row r sits at slot (r % 8) * (d / 8) + r / 8: the 64
+// lanes, reading rows 8 l + j of their 16-byte x slices, hit consecutive slots. The accumulation
+// order is that of route_kernel (lane slices k0 = 8 l + 512 i, j ascending, then the butterfly),
+// so the logits are bit-identical to it.
+constexpr int kRouteLdsMaxD = 4096;
+__global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                                        const float* __restrict__ bias, int64_t ntok, int d, int K,
+                                                        int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                        float* __restrict__ logits) {
+  __shared__ u32x4_t wl[kRouteLdsMaxD];
+  const int d8 = d / 8;
+  for (int r = threadIdx.x; r < d; r += blockDim.x) wl[(r & 7) * d8 + (r >> 3)] = load16(wg + (int64_t)r * 8);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < ntok; t += waves) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll 8
+    for (int k0 = lane * 8; k0 < d; k0 += kWave * 8) {
+      float xv[8];
+      unpack16<bf16_t, 8>(load16(x + t * d + k0), xv);
+      const int r0 = k0 >> 3;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float w[8];
+        unpack16<bf16_t, 8>(wl[j * d8 + r0], w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv[j], w[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = wave_sum(acc[e]);
+    if (lane == 0) finalize_token<8>(acc, t, 8, K, bias, topk_idx, topk_w, logits);
+  }
+}
+
 // Few tokens (decode): one workgroup per token, so all loads of a token are in flight at once.
 // Each of the 256 threads covers 16-byte slices of d; partial sums are reduced across each wave
 // (butterfly) and then across the 4 waves in LDS, in a fixed order.
@@ -215,6 +257,15 @@ void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int 
     launch_kernel((route_token_kernel<T, 8>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
                        static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
     return;
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (E == 8 && d <= kRouteLdsMaxD) {
+      // two workgroups per CU (64 KB of LDS each), a few tokens per wavefront
+      const int64_t blocks = std::min<int64_t>((T_ + 3) / 4, 512);
+      launch_kernel(route_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                    static_cast<const bf16_t*>(wg), bias, T_, d, K, idx, w, logits);
+      return;
+    }
   }
   // one wavefront per token: more wavefronts in flight per CU beat sharing the W_g loads among
   // several tokens (measured at T = 4096: 40 us against 48 us with 4 tokens per wavefront)
