@@ -3,9 +3,9 @@
 // summary, "Método" (n = 8, K = 2).
 //
 // Bandwidth kernel: it reads x once (T*d elements) and W_g (d*E elements, shared by every
-// token and served from L2). One wavefront owns TPW tokens (one at E <= 8: more wavefronts in
-// flight beat sharing the W_g loads); each lane covers 16-byte slices
-// of d and accumulates E partial sums per token in fp32. A butterfly over the 64 lanes gives
+// token: staged in LDS once per workgroup for bf16 with E = 8, else served from L2). One
+// wavefront owns a token at a time; each lane covers 16-byte slices of d and accumulates E
+// partial sums per token in fp32. Decode batches take one workgroup per token instead. A butterfly over the 64 lanes gives
 // every lane the full logits; TopK is then repeated argmax over registers (ties -> lower
 // index) and the softmax uses only the K kept logits, so the other experts get exactly 0.
 #include "common.hpp"
