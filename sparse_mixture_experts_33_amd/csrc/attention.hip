@@ -36,34 +36,35 @@ constexpr int kVRow = kHD + 16;
 
 // qkv [T][(Hq + 2 Hkv) * 128] fp32 -> q [Hq][T][128], k [Hkv][T][128], v [Hkv][T][128] bf16, with the
 // rotary embedding on q and k: in each head the pair (i, i + 64) of position t turns by the angle
-// t * base^(-i/64). One wavefront per (position, head); lane i owns the pair (i, i + 64).
+// t * base^(-i/64). One workgroup per position: thread (i = tid % 64, h0 = tid / 64) owns the pair i
+// of heads h0, h0 + 4, ..., so the angle's sine and cosine are computed once per pair and position.
 __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__ qkv, int64_t T, int Hq, int Hkv,
                                                        double log_base, bf16_t* __restrict__ q,
                                                        bf16_t* __restrict__ k, bf16_t* __restrict__ v) {
-  const int lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x;
+  const int i = threadIdx.x & 63, h0 = threadIdx.x >> 6;
   const int H = Hq + 2 * Hkv;
-  const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  if (item >= T * H) return;
-  const int64_t t = item / H;
-  const int h = (int)(item - t * H);
-  const float* src = qkv + t * (int64_t)H * kHD + (int64_t)h * kHD;
-  float a = src[lane], b = src[lane + 64];
-  bf16_t* dst;
-  if (h < Hq + Hkv) {
-    // angle in double, reduced to [-pi, pi] before the fp32 sine and cosine
-    const double ang = (double)t * exp(-(double)lane / 64.0 * log_base);
-    const double red = ang - 6.283185307179586 * rint(ang / 6.283185307179586);
-    float sn, cs;
-    sincosf((float)red, &sn, &cs);
-    const float ra = a * cs - b * sn, rb = a * sn + b * cs;
-    a = ra;
-    b = rb;
-    dst = h < Hq ? q + ((int64_t)h * T + t) * kHD : k + ((int64_t)(h - Hq) * T + t) * kHD;
-  } else {
-    dst = v + ((int64_t)(h - Hq - Hkv) * T + t) * kHD;
+  // angle in double, reduced to [-pi, pi] before the fp32 sine and cosine
+  const double ang = (double)t * exp(-(double)i / 64.0 * log_base);
+  const double red = ang - 6.283185307179586 * rint(ang / 6.283185307179586);
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  const float* src = qkv + t * (int64_t)H * kHD;
+#pragma unroll 4
+  for (int h = h0; h < H; h += 4) {
+    float a = src[h * kHD + i], b = src[h * kHD + i + 64];
+    bf16_t* dst;
+    if (h < Hq + Hkv) {
+      const float ra = a * cs - b * sn, rb = a * sn + b * cs;
+      a = ra;
+      b = rb;
+      dst = h < Hq ? q + ((int64_t)h * T + t) * kHD : k + ((int64_t)(h - Hq) * T + t) * kHD;
+    } else {
+      dst = v + ((int64_t)(h - Hq - Hkv) * T + t) * kHD;
+    }
+    dst[i] = (bf16_t)f32_to_bf16_rne(a);
+    dst[i + 64] = (bf16_t)f32_to_bf16_rne(b);
   }
-  dst[lane] = (bf16_t)f32_to_bf16_rne(a);
-  dst[lane + 64] = (bf16_t)f32_to_bf16_rne(b);
 }
 
 __device__ inline float max4(f32x4_t v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
@@ -379,8 +380,7 @@ __global__ void set_offsets_kernel(int32_t* off, int32_t T) {
 
 void launch_rope_qkv(const float* qkv, int64_t T, int Hq, int Hkv, double base, void* q, void* k, void* v,
                      hipStream_t s) {
-  const int64_t items = T * (Hq + 2 * Hkv);
-  launch_kernel(rope_qkv_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, qkv, T, Hq, Hkv, std::log(base),
+  launch_kernel(rope_qkv_kernel, dim3((unsigned)T), dim3(256), 0, s, qkv, T, Hq, Hkv, std::log(base),
                 static_cast<bf16_t*>(q), static_cast<bf16_t*>(k), static_cast<bf16_t*>(v));
 }
 
