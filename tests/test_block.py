@@ -49,6 +49,9 @@ ATTN_CASES = {
     "T64": dict(T=64, Hq=4, Hkv=1),
     "T200_g8": dict(T=200, Hq=8, Hkv=1),
     "T577": dict(T=577, Hq=8, Hkv=2),
+    # three and four key tiles: every LDS tile buffer used, then reused
+    "T129_g8": dict(T=129, Hq=8, Hkv=1),
+    "T256_h16": dict(T=256, Hq=16, Hkv=4),
 }
 
 
