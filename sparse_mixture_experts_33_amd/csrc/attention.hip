@@ -160,13 +160,17 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
   for (int d = 0; d < 8; ++d)
 #pragma unroll
     for (int j = 0; j < QJ; ++j) oacc[d][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // running max per query in exponent units (max * scale_log2; all four lanes of a query agree) and
-  // this lane's partial sum of the weights
-  float mrun[QJ], lrun[QJ];
+  // running max per query in exponent units (max * scale_log2; all four lanes of a query agree)
+  float mrun[QJ];
+  // running sum of the weights per query: a 16-row block of the second product whose A operand
+  // is all ones, so every row of it holds sum_k P[k][q] over the bf16 weights that the output
+  // itself is formed from (on the matrix cores, instead of 32 dependent additions per step)
+  f32x4_t lacc[QJ];
+  const u32x4_t ones = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
 #pragma unroll
   for (int j = 0; j < QJ; ++j) {
     mrun[j] = 0.f;
-    lrun[j] = 0.f;
+    lacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   // Scores and the running-max step of tile st (in LDS buffer buf): t = exponents of the weights,
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
         const float dm = st == 0 ? mx : fmaxf(mx, 0.f);
         const float alpha = st == 0 ? 0.f : exp2_hw(-dm);
         mrun[j] += dm;
-        lrun[j] *= alpha;
+        lacc[j] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) oacc[d][j] *= alpha;
 #pragma unroll
@@ -249,15 +253,11 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
     u32x4_t pf[2][QJ];
 #pragma unroll
     for (int j = 0; j < QJ; ++j) {
-      float p[4][4], sum = 0.f;
+      float p[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[i][r] = exp2_hw(t[j][i][r]);
-          sum += p[i][r];
-        }
-      lrun[j] += sum;
+        for (int r = 0; r < 4; ++r) p[i][r] = exp2_hw(t[j][i][r]);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
         pf[kc][j] = u32x4_t{cvt_bf16x2(p[2 * kc][0], p[2 * kc][1]), cvt_bf16x2(p[2 * kc][2], p[2 * kc][3]),
@@ -279,6 +279,10 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
 #pragma unroll
         for (int j = 0; j < QJ; ++j) oacc[d][j] = mfma_bf16(vf, pf[kc][j], oacc[d][j]);
       }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int j = 0; j < QJ; ++j) lacc[j] = mfma_bf16(ones, pf[kc][j], lacc[j]);
   };
 
   // tile 0 in buffer 0 (both phases' rows)
@@ -327,10 +331,7 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
   // O = O^T / sum, rounded to bf16; lane: query q0 + qw + 16 j + li, dims 16 d + 4 g .. +3
 #pragma unroll
   for (int j = 0; j < QJ; ++j) {
-    float l = lrun[j];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / lacc[j][0];
     const int64_t t = q0 + qw + 16 * j + li;
     if (t >= T) continue;
     bf16_t* dst = o + t * (int64_t)Hq * kHD + (int64_t)hq * kHD + 4 * g;
