@@ -527,7 +527,10 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   // average), spread over 256 CUs in rounds of one tile per CU. A split into ks k-ranges turns
   // each round into 1/ks of a round; every extra range costs one more fp32 partial written and
   // read back (8*rows*d bytes at ~6.5 TB/s), expressed in tile times (a 256 x 256 x F tile at
-  // ~4 TFLOP/s per CU). The split depends on the sizes only, so the workspace size does too.
+  // ~4 TFLOP/s per CU), plus a fixed 0.2 tile times (the fill and drain of each range's k-loop
+  // and output; fitted to step times measured with the split forced to 1..4: prefill T = 4096
+  // is fastest at 2, the skewed T = 16384 layer at 1, the T = 2048 stack within 0.5% at 2..4).
+  // The split depends on the sizes only, so the workspace size does too.
   const double per_e = (double)rows / E;
   const double tiles = (double)E * (per_e / 256.0 + 0.5) * (d / 256);
   const double tile_s = 2.0 * 256 * 256 * (double)F / 4.0e12;
@@ -535,7 +538,7 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   int best = 1;
   double best_t = 1e30;
   for (int ks = 1; ks <= kMaxKSplit && F / 64 >= 8 * ks; ++ks) {
-    const double t = std::ceil(tiles * ks / 256.0) / ks + (ks - 1) * part_s / tile_s;
+    const double t = std::ceil(tiles * ks / 256.0) / ks + (ks - 1) * (part_s / tile_s + 0.2);
     if (t < best_t) {
       best_t = t;
       best = ks;
