@@ -3,9 +3,12 @@
 The stack is h <- h + MoE(bf16(h / sqrt(mean(h^2) + eps))), h fp32, unit norm weight (the pages
 describe no norm; this is the workload's own definition). The oracle runs the same stack for
 the selected tokens on its own, in fp64 (tokens are independent in an MoE-only stack, so a sample
-is exact), and never consumes a GPU value. Small numeric differences can flip a routing decision
-whose top-K gap is tiny; a token whose oracle gap fell below MARGIN at some layer is reported and
-left out of the comparison from that layer on.
+is exact), and never consumes a GPU value. The two residual streams drift apart by the bf16
+roundings of every layer, and after many layers the drift can move a token's logits across a
+near-tie, after which the two streams legitimately differ. A token leaves the comparison from the
+layer on where its oracle top-K gap falls below MARGIN, or where the GPU's own routing of its own
+input selects other experts than the oracle's; the latter is accepted only inside the drift band
+(oracle gap below DRIFT_GAP) and fails the test outside it.
 """
 import numpy as np
 import pytest
@@ -17,7 +20,8 @@ from helpers import as_f64, dev, gaps, host, say
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-MARGIN = 1e-2   # logit units: well above the per-layer drift of bf16 rounding of the layer input
+MARGIN = 1e-2     # logit units: well above the per-layer drift of bf16 rounding of the layer input
+DRIFT_GAP = 0.1   # logit units: the most that ~1e-2 relative drift of the stream moves a logit
 
 
 @pytest.fixture(scope="module")
@@ -57,6 +61,9 @@ class Stack:
         self.ws = torch.empty(M.moe_workspace_bytes(self.dims), dtype=torch.uint8, device="cuda")
         self.h_ref = h0[tokens].astype(np.float64)
         self.clean = np.ones(len(tokens), bool)
+        self.idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+        self.wts = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+        self.diverged = 0
 
     def layer(self, l):
         M, w = self.M, self.w
@@ -68,11 +75,17 @@ class Stack:
                 M.moe_pack_weights(self.dims, which, dW[k], out)
                 dW[k] = out
         M.moe_rmsnorm(w.T, w.d, w.eps, self.h, self.x)
+        M.moe_route(self.dims, self.x, dW["w_gate"], self.idx, self.wts)  # the selection moe_forward makes
         M.moe_forward(self.dims, self.x, dW["w_gate"], dW["w1"], dW["w3"], dW["w2"], self.h, self.ws,
                       accumulate=True)
         idx, logits = oracle.deep_layer(self.h_ref, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, w.eps)
-        self.clean &= gaps(logits, w.K)[0] > MARGIN
         torch.cuda.synchronize()
+        gapk = gaps(logits, w.K)[0]
+        same = (np.sort(host(self.idx)[self.tok], axis=1) == np.sort(idx, axis=1)).all(axis=1)
+        outside = self.clean & ~same & (gapk >= DRIFT_GAP)
+        assert not outside.any(), f"layer {l}: tokens {self.tok[outside]} routed differently at gaps {gapk[outside]}"
+        self.diverged += int((self.clean & ~same).sum())
+        self.clean &= same & (gapk > MARGIN)
         got = host(self.h)[self.tok].astype(np.float64)
         ref = self.h_ref
         err = np.abs(got[self.clean] - ref[self.clean]).max() / np.abs(ref[self.clean]).max()
@@ -112,6 +125,7 @@ def test_mixtral_32_layer_stack_sampled(M):
     S = Stack(M, w, tok)
     for l in range(w.layers):
         err = S.layer(l)
-        say(f"  layer {l}: max|d|/max|h_ref| = {err:.3e} over {S.clean.sum()} tokens")
+        say(f"  layer {l}: max|d|/max|h_ref| = {err:.3e} over {S.clean.sum()} tokens "
+            f"({S.diverged} routed apart by drift so far)")
         assert err <= 2e-2
     assert S.clean.sum() >= len(tok) // 2
