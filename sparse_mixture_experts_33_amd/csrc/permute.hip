@@ -31,6 +31,8 @@ __global__ __launch_bounds__(NT) void permute_index_kernel(const int32_t* __rest
   const int64_t s1 = min<int64_t>(S, s0 + chunk);
 
   for (int e = 0; e < E; ++e) cnt[e * NT + i] = 0;
+  // unrolled so that the chunk's loads are in flight together rather than one latency each
+#pragma unroll 8
   for (int64_t s = s0; s < s1; ++s) cnt[topk_idx[s] * NT + i] += 1;
   __syncthreads();
 
@@ -64,11 +66,19 @@ __global__ __launch_bounds__(NT) void permute_index_kernel(const int32_t* __rest
   if (i == 0) offsets[E] = (int)S;
   __syncthreads();
 
-  for (int64_t s = s0; s < s1; ++s) {
-    const int e = topk_idx[s];
-    const int row = cnt[e * NT + i]++;
-    row_token[row] = (int32_t)(s / K);
-    token_row[s] = row;
+  // eight slot ids loaded together, then handed out in slot order
+  for (int64_t s = s0; s < s1; s += 8) {
+    int e8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) e8[u] = topk_idx[min(s + u, s1 - 1)];  // clamped: loads need no branch
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s + u < s1) {
+        const int row = cnt[e8[u] * NT + i]++;
+        row_token[row] = (int32_t)((s + u) / K);
+        token_row[s + u] = row;
+      }
+    }
   }
 }
 
