@@ -377,55 +377,59 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         if (s + 3 < s1) dma(s + 3);
         const uint32_t st = (uint32_t)(s & 3) * SB;
         const uint32_t av = aoff + st, bv = boff + st;
-        // weight blocks wblock(0..7) (SwiGLU: 4 of w1, then the same 4 of w3, 8 blocks apart) and
-        // token blocks wt + 4b; early-clobber outputs, since the reads are in flight together
-        u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3;
-        if constexpr (SWIGLU) {
-          asm volatile(
-              "ds_read_b128 %0, %12 offset:0\n"
-              "ds_read_b128 %1, %12 offset:1024\n"
-              "ds_read_b128 %2, %12 offset:2048\n"
-              "ds_read_b128 %3, %12 offset:3072\n"
-              "ds_read_b128 %4, %12 offset:8192\n"
-              "ds_read_b128 %5, %12 offset:9216\n"
-              "ds_read_b128 %6, %12 offset:10240\n"
-              "ds_read_b128 %7, %12 offset:11264\n"
-              "ds_read_b128 %8, %13 offset:0\n"
-              "ds_read_b128 %9, %13 offset:4096\n"
-              "ds_read_b128 %10, %13 offset:8192\n"
-              "ds_read_b128 %11, %13 offset:12288\n"
-              "s_waitcnt lgkmcnt(0)\n"
-              : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
-                "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
-              : "v"(av), "v"(bv)
-              : "memory");
-        } else {
-          asm volatile(
-              "ds_read_b128 %0, %12 offset:0\n"
-              "ds_read_b128 %1, %12 offset:1024\n"
-              "ds_read_b128 %2, %12 offset:2048\n"
-              "ds_read_b128 %3, %12 offset:3072\n"
-              "ds_read_b128 %4, %12 offset:4096\n"
-              "ds_read_b128 %5, %12 offset:5120\n"
-              "ds_read_b128 %6, %12 offset:6144\n"
-              "ds_read_b128 %7, %12 offset:7168\n"
-              "ds_read_b128 %8, %13 offset:0\n"
-              "ds_read_b128 %9, %13 offset:4096\n"
-              "ds_read_b128 %10, %13 offset:8192\n"
-              "ds_read_b128 %11, %13 offset:12288\n"
-              "s_waitcnt lgkmcnt(0)\n"
-              : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
-                "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
-              : "v"(av), "v"(bv)
-              : "memory");
-        }
-        const u32x4_t A[8] = {A0, A1, A2, A3, A4, A5, A6, A7};
-        const u32x4_t B[4] = {B0, B1, B2, B3};
+        // a wavefront whose token blocks are all past the group's end (in the last, partly filled
+        // tile) skips its fragment reads as well as its MFMAs
+        if (decltype(full)::value || nbv > 0) {
+          // weight blocks wblock(0..7) (SwiGLU: 4 of w1, then the same 4 of w3, 8 blocks apart) and
+          // token blocks wt + 4b; early-clobber outputs, since the reads are in flight together
+          u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3;
+          if constexpr (SWIGLU) {
+            asm volatile(
+                "ds_read_b128 %0, %12 offset:0\n"
+                "ds_read_b128 %1, %12 offset:1024\n"
+                "ds_read_b128 %2, %12 offset:2048\n"
+                "ds_read_b128 %3, %12 offset:3072\n"
+                "ds_read_b128 %4, %12 offset:8192\n"
+                "ds_read_b128 %5, %12 offset:9216\n"
+                "ds_read_b128 %6, %12 offset:10240\n"
+                "ds_read_b128 %7, %12 offset:11264\n"
+                "ds_read_b128 %8, %13 offset:0\n"
+                "ds_read_b128 %9, %13 offset:4096\n"
+                "ds_read_b128 %10, %13 offset:8192\n"
+                "ds_read_b128 %11, %13 offset:12288\n"
+                "s_waitcnt lgkmcnt(0)\n"
+                : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
+                  "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
+                : "v"(av), "v"(bv)
+                : "memory");
+          } else {
+            asm volatile(
+                "ds_read_b128 %0, %12 offset:0\n"
+                "ds_read_b128 %1, %12 offset:1024\n"
+                "ds_read_b128 %2, %12 offset:2048\n"
+                "ds_read_b128 %3, %12 offset:3072\n"
+                "ds_read_b128 %4, %12 offset:4096\n"
+                "ds_read_b128 %5, %12 offset:5120\n"
+                "ds_read_b128 %6, %12 offset:6144\n"
+                "ds_read_b128 %7, %12 offset:7168\n"
+                "ds_read_b128 %8, %13 offset:0\n"
+                "ds_read_b128 %9, %13 offset:4096\n"
+                "ds_read_b128 %10, %13 offset:8192\n"
+                "ds_read_b128 %11, %13 offset:12288\n"
+                "s_waitcnt lgkmcnt(0)\n"
+                : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
+                  "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
+                : "v"(av), "v"(bv)
+                : "memory");
+          }
+          const u32x4_t A[8] = {A0, A1, A2, A3, A4, A5, A6, A7};
+          const u32x4_t B[4] = {B0, B1, B2, B3};
 #pragma unroll
-        for (int b = 0; b < BB; ++b) {
-          if (decltype(full)::value || b < nbv) {
+          for (int b = 0; b < BB; ++b) {
+            if (decltype(full)::value || b < nbv) {
 #pragma unroll
-            for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+              for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+            }
           }
         }
       }
