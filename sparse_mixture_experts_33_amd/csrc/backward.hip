@@ -138,9 +138,17 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float rsum = 0.0f;
+      if (EMAX == 8 && E == 8) {
+        // the row's 8 gate weights in one 16-byte load; same order of products as below
+        const u32x4_t wr = load16(w_gate + (int64_t)(c + q) * 8);
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e)
-        if (e < E) rsum = fmaf(Elem<bf16_t>::to_f32(w_gate[(int64_t)(c + q) * E + e]), dl[e], rsum);
+        for (int e = 0; e < 8; ++e)
+          rsum = fmaf((e & 1) ? bf16_hi(wr[e >> 1]) : bf16_lo(wr[e >> 1]), dl[e], rsum);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+          if (e < E) rsum = fmaf(Elem<bf16_t>::to_f32(w_gate[(int64_t)(c + q) * E + e]), dl[e], rsum);
+      }
       s[q] += rsum;
     }
     *reinterpret_cast<f32x4_t*>(dx + t * d + c) = s;
