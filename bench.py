@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--probe", choices=["copy"], help="plain copy of known size (counter calibration)")
-    p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "block"], default="forward",
+    p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "train", "block"], default="forward",
                    help="time moe_forward (default), moe_backward (gradients of the layer) or moe_block_forward "
                         "(decoder block: attention and the layer; workloads block_T*)")
     return p.parse_args()
@@ -107,8 +107,8 @@ def main():
         return
 
     w = mi.WORKLOADS[args.workload]
-    if args.pass_ == "backward":
-        backward_bench(args, w)
+    if args.pass_ in ("backward", "train"):
+        backward_bench(args, w, train=args.pass_ == "train")
         return
     if args.pass_ == "block":
         block_bench(args, w)
@@ -266,9 +266,14 @@ def main():
 BWD_METRIC = "MoE-layer backward tokens/s + TFLOP/s vs peak (E=8,K=2,d=4096,F=14336)"
 
 
-def backward_bench(args, w):
+TRAIN_METRIC = "MoE-layer training-step tokens/s (forward keeping activations + backward) + TFLOP/s vs peak"
+
+
+def backward_bench(args, w, train=False):
     """One step = one moe_backward call (routing and expert pre-activations recomputed from x; dx,
-    dW_g, dw1, dw3, dw2 in fp32) over the workload's tokens, inputs resident in HBM."""
+    dW_g, dw1, dw3, dw2 in fp32) over the workload's tokens, inputs resident in HBM.
+    train: one step = moe_forward keeping the expert pre-activations (moe_opts.activations) and
+    moe_backward reading them, row-major weights (the single copy both calls take)."""
     import numpy as np
     import torch
 
@@ -295,10 +300,20 @@ def backward_bench(args, w):
     dw2 = torch.empty((w.E, w.d, w.F), **f32)
     ws = torch.empty(moe.moe_backward_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    act = torch.empty((2 * w.T * w.K * w.F,), **f32) if train else None
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda") if train else None
+    fws = torch.empty(moe.moe_workspace_bytes(dims), dtype=torch.uint8, device="cuda") if train else None
+    mid = [(torch.cuda.Event(enable_timing=True)) for _ in range(args.steps + args.warmup)] if train else None
+    it = [0]
 
     def step():
+        if train:
+            moe.moe_forward(dims, x, L["w_gate"], L["w1"], L["w3"], L["w2"], y, fws, gate_bias=L["bias"],
+                            activations=act)
+            mid[it[0]].record(stream)
+            it[0] += 1
         moe.moe_backward(dims, x, L["w_gate"], L["w1"], L["w3"], L["w2"], dy, dx, dwg, dw1, dw3, dw2, ws,
-                         gate_bias=L["bias"])
+                         gate_bias=L["bias"], activations=act)
 
     for _ in range(args.warmup):
         step()
@@ -315,12 +330,16 @@ def backward_bench(args, w):
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # algorithmic work of a backward pass: the gradient products w2^T dy, [w1|w3]^T [da|db] and the
     # three weight gradients (6 T*K*d*F multiply-adds, twice the forward), plus the router's two
-    # T*d*E products. The recomputed forward products are implementation work, not counted.
+    # T*d*E products. The recomputed forward products are implementation work, not counted. A
+    # training step adds the forward's 6 T*K*d*F + 2 T*d*E.
     S = w.T * w.K
     flops = 12 * S * w.d * w.F + 4 * w.T * w.d * w.E
+    if train:
+        flops += 6 * S * w.d * w.F + 2 * w.T * w.d * w.E
+        fwd_ms = float(np.mean([a.elapsed_time(m) for (a, _), m in zip(ev, mid[args.warmup:])]))
     tf = flops / (call_ms * 1e-3) / 1e12
     out = {
-        "metric": BWD_METRIC,
+        "metric": TRAIN_METRIC if train else BWD_METRIC,
         "value": round(w.T * args.steps / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -332,20 +351,27 @@ def backward_bench(args, w):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens and upstream gradient, N(0,1/fan_in) weights)",
-        "config": {"workload": w.name, "pass": "backward", "T": w.T, "d": w.d, "F": w.F, "E": w.E, "K": w.K,
-                   "weight_layout": "row-major", "parallelism": "single GPU"},
+        "config": {"workload": w.name, "pass": "train" if train else "backward", "T": w.T, "d": w.d, "F": w.F,
+                   "E": w.E, "K": w.K, "weight_layout": "row-major", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "moe_backward, whole call (HIP events around each call)", "kernel_ms": round(call_ms, 4),
+                     "kernel": ("moe_forward + moe_backward, whole step" if train else "moe_backward, whole call")
+                     + " (HIP events around each call)", "kernel_ms": round(call_ms, 4),
                      "algorithmic": {"flops": flops}},
         "cpu_baseline": None,
     }
+    if train:
+        out["forward_ms"] = round(fwd_ms, 4)
+        out["backward_ms"] = round(call_ms - fwd_ms, 4)
     if not args.no_cpu_baseline:
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
         sample = np.linspace(0, w.T - 1, 16).astype(np.int64)
         done, reps, t1 = 0, 0, time.perf_counter()
         while True:
+            if train:
+                oracle.forward(x_host, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, bias=W["bias"], tokens=sample,
+                               threads=threads)
             oracle.backward_tokens(x_host, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, dy_host.astype(np.float64),
                                    sample, bias=W["bias"], threads=threads)
             done += len(sample)
@@ -354,7 +380,8 @@ def backward_bench(args, w):
                 break
         el = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": f"dx and logit gradients of {len(sample)} tokens x {reps} repetitions "
+                               "sample": ("forward outputs, " if train else "") +
+                                         f"dx and logit gradients of {len(sample)} tokens x {reps} repetitions "
                                          f"({el:.1f}s; the weight-gradient sums are not included)"}
     print(json.dumps(out), flush=True)
 

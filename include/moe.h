@@ -94,13 +94,23 @@ typedef struct {
                                 stage s's kernel, taken from the dispatch itself (no extra queue
                                 packets, so timing does not slow the step). NULL entries are
                                 skipped; with T = 0 nothing is launched or recorded. */
+  float* activations;        /* optional, for training, or NULL: [2][T*K][F] fp32 = the expert
+                                pre-activations a = x . w1[e]^T (first half) and b = x . w3[e]^T
+                                (second half) of every routed row, rows in the permuted order of
+                                moe_permute. moe_forward writes them (computing the expert
+                                product a, b in fp32 and h = silu(a) b from them, the same h as
+                                without them on the tiled path); moe_backward given the same x,
+                                w_gate, gate_bias and weights reads them instead of recomputing
+                                them. Needs dims->dtype = MOE_BF16 and d, F multiples of 256. */
 } moe_opts;
 
 /* Stages of moe_forward, in launch order (one kernel each). */
 enum {
   MOE_STAGE_ROUTE = 0,       /* logits, TopK, softmax */
   MOE_STAGE_PERMUTE = 1,     /* counts, offsets, stable row maps */
-  MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1) */
+  MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1; with
+                                opts->activations, from the start of the product to the end of
+                                the separate SwiGLU kernel) */
   MOE_STAGE_EXPERT_DOWN = 3, /* hidden x w2 (grouped GEMM 2) */
   MOE_STAGE_COMBINE = 4,     /* gate-weighted sum back to token order */
   MOE_NUM_STAGES = 5,
@@ -191,7 +201,8 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
  *   dh_k = w2[e_k]^T (g_k dy),  da_k = dh_k * b_k * silu'(a_k),  db_k = dh_k * silu(a_k)
  *   dx   = sum_k (w1[e_k]^T da_k + w3[e_k]^T db_k) + W_g dlogit
  *   dw2[e] = sum (g_k dy) h_k^T,  dw1[e] = sum da_k x^T,  dw3[e] = sum db_k x^T,  dW_g = x^T dlogit
- * The routing and a_k, b_k are recomputed from x (nothing is kept from the forward call).
+ * The routing is recomputed from x; a_k, b_k are too, unless opts->activations holds them from a
+ * moe_forward call on the same inputs.
  *   x, w_gate, w1, w3, w2  as in moe_forward (dims->dtype = MOE_BF16, weights row-major)
  *   dy       [T][d]    fp32 in   gradient of the loss with respect to y
  *   dx       [T][d]    fp32 out
@@ -203,7 +214,8 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
  *   workspace: >= moe_backward_workspace_bytes(dims) bytes of device memory, 256-byte aligned
  * Operands of the matrix products are bf16 (dy, g_k dy, h_k, da_k and db_k rounded to nearest
  * even); all sums are fp32 in a fixed order, so results are reproducible bit for bit.
- * opts: gate_bias as in the forward; y_dtype, accumulate and stage_events are ignored.
+ * opts: gate_bias and activations as in the forward; y_dtype, accumulate and stage_events are
+ * ignored.
  * Supported: dims->dtype = MOE_BF16, weight_layout = MOE_LAYOUT_ROWMAJOR, d and F multiples of 256
  * (with the general limits above); other valid arguments return MOE_ERR_UNSUPPORTED. */
 size_t moe_backward_workspace_bytes(const moe_dims* dims);

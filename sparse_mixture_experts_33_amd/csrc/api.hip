@@ -147,7 +147,19 @@ moe_status check_backward_sizes(const moe_dims& m) {
   return MOE_OK;
 }
 
-const moe_opts kDefaultOpts = {nullptr, -1, 0, nullptr};
+const moe_opts kDefaultOpts = {nullptr, -1, 0, nullptr, nullptr};
+
+// Saved expert pre-activations (moe_opts.activations): the tiled product that writes them needs
+// bf16 and d, F multiples of 256.
+moe_status check_activations(const moe_dims& m, const moe_opts* o) {
+  if (!o || !o->activations) return MOE_OK;
+  if (!aligned16(o->activations)) return fail(MOE_ERR_INVALID_ARG, "activations is not 16-byte aligned");
+  if (m.dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "saved activations need bf16 (dtype = %d)", m.dtype);
+  if (m.d % 256 != 0 || m.F % 256 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "saved activations need d and F multiples of 256 (d = %d, F = %d)", m.d, m.F);
+  return MOE_OK;
+}
 
 moe_status check_attn(const moe_attn_dims* a) {
   if (!a) return fail(MOE_ERR_INVALID_ARG, "attn is NULL");
@@ -221,7 +233,7 @@ moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -347,6 +359,7 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   const moe_dims& m = *dims;
   int yd = 0;
   MOE_TRY(check_opts(m, opts, &yd));
+  MOE_TRY(check_activations(m, opts));
   if (m.T == 0) return MOE_OK;
   const Workspace L = layout(m);
   MOE_TRY(check_ptr(workspace, "workspace"));
@@ -394,8 +407,19 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (permute)"));
-  arm(MOE_STAGE_EXPERT_UP);
-  moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);
+  float* act = opts ? opts->activations : nullptr;
+  if (act) {
+    // training: the pre-activations a, b in fp32 (kept for the backward pass), then h from them
+    float* a = act;
+    float* b = act + (size_t)m.T * m.K * m.F;
+    if (ev) moe::pending_dispatch_events() = {static_cast<hipEvent_t>(ev[2 * MOE_STAGE_EXPERT_UP]), nullptr};
+    moe::launch_tile_up_pair(m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, a, b, s);
+    if (ev) moe::pending_dispatch_events() = {nullptr, static_cast<hipEvent_t>(ev[2 * MOE_STAGE_EXPERT_UP + 1])};
+    moe::launch_swiglu_h(a, b, m.T * m.K, m.F, h, s);
+  } else {
+    arm(MOE_STAGE_EXPERT_UP);
+    moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);
+  }
   MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (expert up)"));
   arm(MOE_STAGE_EXPERT_DOWN);
@@ -437,6 +461,7 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   if (dlogits && !aligned16(dlogits)) return fail(MOE_ERR_INVALID_ARG, "dlogits is not 16-byte aligned");
   int yd = 0;
   MOE_TRY(check_opts(m, opts, &yd));
+  MOE_TRY(check_activations(m, opts));
   if (m.T == 0) return MOE_OK;
   const BwdWorkspace L = bwd_layout(m);
   MOE_TRY(check_ptr(workspace, "workspace"));
@@ -453,8 +478,9 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
   int32_t* row_token = static_cast<int32_t*>(at(L.row_token));
   int32_t* token_row = static_cast<int32_t*>(at(L.token_row));
-  float* A = static_cast<float*>(at(L.A));
-  float* B = static_cast<float*>(at(L.B));
+  const float* saved = opts ? opts->activations : nullptr;
+  float* A = saved ? const_cast<float*>(saved) : static_cast<float*>(at(L.A));
+  float* B = saved ? const_cast<float*>(saved) + (size_t)m.T * m.K * m.F : static_cast<float*>(at(L.B));
   float* dhp = static_cast<float*>(at(L.dhp));
   float* dg = static_cast<float*>(at(L.dg));
   float* dlog = dlogits ? dlogits : static_cast<float*>(at(L.dlog));
@@ -470,7 +496,7 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
                     nullptr, s);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
-  moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
+  if (!saved) moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // dh' = w2^T dy per row (w2 [E][d][F] is the transposed weight of this product), then the SwiGLU
   // and softmax derivatives

@@ -97,6 +97,8 @@ void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, h
 // dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]) for row r = (t, k) with gate g.
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t stream);
+// h = bf16(silu(A) B) elementwise over rows x F (the forward's hidden vector from saved pre-activations).
+void launch_swiglu_h(const float* A, const float* B, int64_t rows, int F, void* h, hipStream_t stream);
 // h = bf16(silu(A) B), dg = dh' . h, dab = [bf16(g dh' B silu'(A)) | bf16(g dh' silu(A))] per row.
 void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,
                        const int32_t* token_row, const float* topk_w, int K, int64_t rows, int F, void* h, void* dab,

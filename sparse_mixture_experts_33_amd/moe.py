@@ -42,7 +42,7 @@ class moe_dims(ctypes.Structure):
 
 class moe_opts(ctypes.Structure):
     _fields_ = [("gate_bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("activations", ctypes.c_void_p)]
 
 
 class moe_attn_dims(ctypes.Structure):
@@ -142,9 +142,9 @@ def _check(status: int):
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16, stage_events=None):
+def _opts(gate_bias=None, y_dtype=None, accumulate=False, dtype=MOE_BF16, stage_events=None, activations=None):
     return moe_opts(_ptr(gate_bias), dtype if y_dtype is None else y_dtype, 1 if accumulate else 0,
-                    stage_events)
+                    stage_events, _ptr(activations))
 
 
 def stage_event_array(events: dict, stages: int = MOE_NUM_STAGES):
@@ -191,10 +191,12 @@ def moe_workspace_bytes(dims: Dims) -> int:
 
 
 def moe_forward(dims: Dims, x, w_gate, w1, w3, w2, y, workspace, gate_bias=None, y_dtype=None, accumulate=False,
-                stream=None, workspace_bytes=None, stage_events=None):
-    """stage_events: None or the result of stage_event_array() (kept alive by the caller)."""
+                stream=None, workspace_bytes=None, stage_events=None, activations=None):
+    """stage_events: None or the result of stage_event_array() (kept alive by the caller).
+    activations: None or an fp32 device tensor of 2*T*K*F elements that receives the expert
+    pre-activations for moe_backward (moe_opts.activations)."""
     o = _opts(gate_bias, y_dtype, accumulate, dims.dtype,
-              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p).value)
+              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p).value, activations)
     nbytes = workspace_bytes if workspace_bytes is not None else (
         workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
     _check(lib().moe_forward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
@@ -206,9 +208,11 @@ def moe_backward_workspace_bytes(dims: Dims) -> int:
 
 
 def moe_backward(dims: Dims, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2, workspace, dlogits=None,
-                 gate_bias=None, stream=None, workspace_bytes=None):
-    """Gradients of the layer (include/moe.h, moe_backward). dy and every output are fp32 device tensors."""
-    o = _opts(gate_bias, dtype=dims.dtype)
+                 gate_bias=None, stream=None, workspace_bytes=None, activations=None):
+    """Gradients of the layer (include/moe.h, moe_backward). dy and every output are fp32 device tensors.
+    activations: None (recompute the expert pre-activations) or the tensor a moe_forward call on
+    the same inputs filled."""
+    o = _opts(gate_bias, dtype=dims.dtype, activations=activations)
     nbytes = workspace_bytes if workspace_bytes is not None else (
         workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
     _check(lib().moe_backward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
     assert [moe.moe_status_string(i) for i in range(5)] == list(moe.moe.STATUS.values())
 
 
@@ -98,6 +98,27 @@ def test_workspace_checks():
                          None) == 1
     acc = moe_opts(None, 0, 2)
     assert L.moe_combine(ctypes.byref(d), ctypes.byref(acc), FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_saved_activations_validation():
+    """moe_opts.activations: 16-byte aligned, bf16, d and F multiples of 256 (forward and backward)."""
+    L = moe.lib()
+    d = moe_dims(32, 4096, 14336, 8, 2, 1)
+    need = moe.moe_workspace_bytes(moe.Dims(32, 4096, 14336, 8, 2, 1))
+    fwd = lambda dims, o, nbytes: L.moe_forward(ctypes.byref(dims), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, nbytes, None)
+    ok = moe_opts(None, 1, 0, None, FAKE)
+    assert fwd(d, ok, need - 1) == 3                                   # accepted, then the workspace check
+    assert fwd(d, moe_opts(None, 1, 0, None, FAKE + 4), need) == 1     # misaligned
+    assert "activations" in moe.moe_last_error()
+    f32 = moe_dims(32, 4096, 14336, 8, 2, 0)
+    assert fwd(f32, moe_opts(None, 0, 0, None, FAKE), moe.moe_workspace_bytes(moe.Dims(32, 4096, 14336, 8, 2, 0))) == 2
+    d192 = moe_dims(32, 192, 512, 8, 2, 1)
+    assert fwd(d192, ok, moe.moe_workspace_bytes(moe.Dims(32, 192, 512, 8, 2, 1))) == 2
+    bwd = moe_dims(64, 256, 512, 8, 2, 1, 0)
+    bad = moe_opts(None, 1, 0, None, FAKE + 4)
+    assert L.moe_backward(ctypes.byref(bwd), ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, None, FAKE, 1 << 40, None) == 1
 
 
 def test_rmsnorm_validation():
