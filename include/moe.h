@@ -268,8 +268,8 @@ moe_status moe_attention(const moe_attn_dims* attn, const void* q, const void* k
  *   moe->T and moe->d must equal attn->T and attn->d. opts: gate_bias as for moe_forward;
  *   stage_events, if not NULL, an array of 2 * MOE_BLOCK_NUM_STAGES events: entries 0 .. 2 *
  *   MOE_NUM_STAGES - 1 time the layer's stages as in moe_forward, entries 2 * MOE_STAGE_ATTENTION
- *   and 2 * MOE_STAGE_ATTENTION + 1 the attention kernel; y_dtype and accumulate are ignored
- *   (the layer's output is added to h).
+ *   and 2 * MOE_STAGE_ATTENTION + 1 the attention kernel; y_dtype, accumulate and activations are
+ *   ignored (the layer's output is added to h).
  *   workspace: >= moe_block_workspace_bytes() bytes of device memory, 256-byte aligned.
  * Supported: bf16, head_dim 128, n_heads a multiple of 4 * n_kv_heads, d a multiple of 256
  * (with the layer's limits). */

@@ -582,6 +582,7 @@ moe_status moe_block_forward(const moe_dims* dims, const moe_attn_dims* attn, co
   moe_opts o2 = opts ? *opts : kDefaultOpts;
   o2.accumulate = 1;
   o2.y_dtype = MOE_F32;
+  o2.activations = nullptr;  // the block keeps no activations (documented as ignored)
   return moe_forward(dims, &o2, at_(L.x2), w_gate, w1, w3, w2, h, at_(L.moe), layout(*dims).total, stream);
 }
 
