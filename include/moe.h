@@ -97,9 +97,9 @@ typedef struct {
   float* activations;        /* optional, for training, or NULL: [2][T*K][F] fp32 = the expert
                                 pre-activations a = x . w1[e]^T (first half) and b = x . w3[e]^T
                                 (second half) of every routed row, rows in the permuted order of
-                                moe_permute. moe_forward writes them (computing the expert
-                                product a, b in fp32 and h = silu(a) b from them, the same h as
-                                without them on the tiled path); moe_backward given the same x,
+                                moe_permute. moe_forward writes them (its expert product
+                                stores a, b in fp32 besides h = silu(a) b, the same h as without
+                                them on the tiled path); moe_backward given the same x,
                                 w_gate, gate_bias and weights reads them instead of recomputing
                                 them. Needs dims->dtype = MOE_BF16 and d, F multiples of 256. */
 } moe_opts;
@@ -108,9 +108,7 @@ typedef struct {
 enum {
   MOE_STAGE_ROUTE = 0,       /* logits, TopK, softmax */
   MOE_STAGE_PERMUTE = 1,     /* counts, offsets, stable row maps */
-  MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1; with
-                                opts->activations, from the start of the product to the end of
-                                the separate SwiGLU kernel) */
+  MOE_STAGE_EXPERT_UP = 2,   /* gathered rows x w1, w3 and the SwiGLU product (grouped GEMM 1) */
   MOE_STAGE_EXPERT_DOWN = 3, /* hidden x w2 (grouped GEMM 2) */
   MOE_STAGE_COMBINE = 4,     /* gate-weighted sum back to token order */
   MOE_NUM_STAGES = 5,

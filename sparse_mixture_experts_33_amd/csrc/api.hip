@@ -409,13 +409,11 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   MOE_TRY(check_launch("moe_forward (permute)"));
   float* act = opts ? opts->activations : nullptr;
   if (act) {
-    // training: the pre-activations a, b in fp32 (kept for the backward pass), then h from them
+    // training: the pre-activations a, b in fp32 (kept for the backward pass) and h, in one product
     float* a = act;
     float* b = act + (size_t)m.T * m.K * m.F;
-    if (ev) moe::pending_dispatch_events() = {static_cast<hipEvent_t>(ev[2 * MOE_STAGE_EXPERT_UP]), nullptr};
-    moe::launch_tile_up_pair(m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, a, b, s);
-    if (ev) moe::pending_dispatch_events() = {nullptr, static_cast<hipEvent_t>(ev[2 * MOE_STAGE_EXPERT_UP + 1])};
-    moe::launch_swiglu_h(a, b, m.T * m.K, m.F, h, s);
+    arm(MOE_STAGE_EXPERT_UP);
+    moe::launch_tile_up_pair(m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, a, b, s, h);
   } else {
     arm(MOE_STAGE_EXPERT_UP);
     moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);

@@ -53,19 +53,6 @@ __global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict_
   }
 }
 
-// h = bf16(silu(a) b) over rows x F, 4 elements per thread: the hidden vector of the forward pass
-// from its saved fp32 pre-activations, with the arithmetic of the fused SwiGLU epilogue (silu(z) =
-// z / (1 + e^-z), product, one rounding to nearest even), so h is the same as the fused product's.
-__global__ __launch_bounds__(256) void swiglu_h_kernel(const float* __restrict__ A, const float* __restrict__ B,
-                                                       int64_t n4, bf16_t* __restrict__ h) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(A + 4 * i);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(B + 4 * i);
-  *reinterpret_cast<u32x2_t*>(h + 4 * i) = u32x2_t{pack_bf16x2(silu_f(a[0]) * b[0], silu_f(a[1]) * b[1]),
-                                                   pack_bf16x2(silu_f(a[2]) * b[2], silu_f(a[3]) * b[3])};
-}
-
 // Per row r: from the recomputed pre-activations a = A[r], b = B[r] and dh' = DHP[r] (fp32):
 // h = bf16(silu(a) b) (as the forward stores it), dg[r] = sum_f dh'_f h_f (fixed order),
 // dab[r] = [bf16(da) | bf16(db)] with da = g dh' b silu'(a), db = g dh' silu(a). One block per row.
@@ -209,12 +196,6 @@ void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* 
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t s) {
   launch_kernel(gather_dy_kernel, dim3((unsigned)rows), dim3(256), 0, s, dy, row_token, token_row, topk_w, K, d,
                 static_cast<bf16_t*>(dy_perm), static_cast<bf16_t*>(do_perm));
-}
-
-void launch_swiglu_h(const float* A, const float* B, int64_t rows, int F, void* h, hipStream_t s) {
-  const int64_t n4 = rows * (int64_t)F / 4;  // F is a multiple of 4
-  launch_kernel(swiglu_h_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, A, B, n4,
-                static_cast<bf16_t*>(h));
 }
 
 void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,

@@ -72,9 +72,11 @@ void launch_tile_up(int layout, const void* act, const int32_t* row_src, const i
 // K of 64 (of 128 with wb).
 void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
                     const void* wb, float* out, int ksplit, float* part, hipStream_t stream);
-// Backward pass: the two pre-activations a = x.w1^T, b = x.w3^T (fp32) in one pass of the up tile.
+// The two pre-activations a = x.w1^T, b = x.w3^T (fp32) in one pass of the up tile, and, if h is
+// not null, h = bf16(silu(a) b) as the fused product forms it (the forward keeping activations).
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
-                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream);
+                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream,
+                         void* h = nullptr);
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
 
@@ -97,8 +99,6 @@ void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, h
 // dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]) for row r = (t, k) with gate g.
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t stream);
-// h = bf16(silu(A) B) elementwise over rows x F (the forward's hidden vector from saved pre-activations).
-void launch_swiglu_h(const float* A, const float* B, int64_t rows, int F, void* h, hipStream_t stream);
 // h = bf16(silu(A) B), dg = dh' . h, dab = [bf16(g dh' B silu'(A)) | bf16(g dh' silu(A))] per row.
 void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,
                        const int32_t* token_row, const float* topk_w, int K, int64_t rows, int F, void* h, void* dab,

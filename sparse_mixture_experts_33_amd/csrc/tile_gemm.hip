@@ -74,7 +74,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ wa,
                                                            const bf16_t* __restrict__ wb, OutT* __restrict__ out,
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
-                                                           int64_t part_stride, int M, int ldw) {
+                                                           int64_t part_stride, int M, int ldw,
+                                                           bf16_t* __restrict__ hout) {
   static_assert(!WGRAD || (!SWIGLU && !PACKED && WT), "the weight-gradient mode reads both operands k-major");
   static_assert(!WT || (!SWIGLU && !PACKED), "transposed weights: plain product only");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
@@ -478,6 +479,12 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         const f32x4_t& v = acc[a + AB / 2][b];
         store16(part + o, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                                   __float_as_uint(v[3])});
+        if (hout) {  // and h = bf16(silu(a) b), as the fused epilogue below forms it
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = silu_t(acc[a][b][q]) * v[q];
+          *reinterpret_cast<u32x2_t*>(hout + o) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        }
       }
   } else if constexpr (SWIGLU) {
 #pragma unroll
@@ -509,13 +516,15 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
 template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false>
 void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
-                 const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s) {
+                 const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s,
+                 void* hout = nullptr) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
   launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
-                static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0, N);
+                static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0, N,
+                static_cast<bf16_t*>(hout));
 }
 
 }  // namespace
@@ -558,7 +567,7 @@ void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int 
   launch_kernel((tile_gemm_kernel<256, 256, false, false, true, true, float>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(p), static_cast<const int32_t*>(nullptr), offsets,
                 static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(nullptr), out, ldp, N, E, 1,
-                static_cast<float*>(nullptr), (int64_t)0, M, ldq);
+                static_cast<float*>(nullptr), (int64_t)0, M, ldq, static_cast<bf16_t*>(nullptr));
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
@@ -570,11 +579,12 @@ void launch_tile_up(int layout, const void* act, const int32_t* row_src, const i
 }
 
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
-                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s) {
+                         int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s,
+                         void* h) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
+    launch_tile<256, 256, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
   else
-    launch_tile<256, 256, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s);
+    launch_tile<256, 256, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
 }
 
 void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
