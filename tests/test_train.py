@@ -38,10 +38,13 @@ CASES = {
     # small groups: the regular forward streams the weights
     "stream_e8": dict(w=mi.Workload("train_stream_e8", T=200, d=256, F=512, dtype="bf16", seed=813),
                       tiled=False, packed=False),
+    # more experts, four kept, and a router bias (the routing both calls recompute must agree)
+    "e16_k4_bias": dict(w=mi.Workload("train_e16_k4", T=600, d=256, F=256, E=16, K=4, dtype="bf16", seed=814),
+                        tiled=False, packed=False, bias=True),
 }
 
 
-def run(M, w, W, x, packed, keep):
+def run(M, w, W, x, packed, keep, bias=None):
     """moe_forward (optionally keeping the activations), then moe_backward with or without them."""
     layout = M.MOE_LAYOUT_PACKED if packed else M.MOE_LAYOUT_ROWMAJOR
     dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16, layout)
@@ -56,7 +59,8 @@ def run(M, w, W, x, packed, keep):
     act = torch.full((2 * w.T * w.K * w.F,), float("nan"), dtype=torch.float32, device="cuda") if keep else None
     y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
-    M.moe_forward(dm, xd, fw["w_gate"], fw["w1"], fw["w3"], fw["w2"], y, ws, activations=act)
+    b = None if bias is None else dev(bias)
+    M.moe_forward(dm, xd, fw["w_gate"], fw["w1"], fw["w3"], fw["w2"], y, ws, gate_bias=b, activations=act)
     # the backward pass takes row-major weights
     db = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16)
     bws = torch.empty(M.moe_backward_workspace_bytes(db), dtype=torch.uint8, device="cuda")
@@ -66,7 +70,7 @@ def run(M, w, W, x, packed, keep):
          "dw2": torch.empty((w.E, w.d, w.F), **f32), "dlogits": torch.empty((w.T, w.E), **f32)}
     dy = dev(mi.upstream_grad(w))
     M.moe_backward(db, xd, dW["w_gate"], dW["w1"], dW["w3"], dW["w2"], dy, g["dx"], g["dw_gate"], g["dw1"],
-                   g["dw3"], g["dw2"], bws, dlogits=g["dlogits"], activations=act)
+                   g["dw3"], g["dw2"], bws, dlogits=g["dlogits"], gate_bias=b, activations=act)
     torch.cuda.synchronize()
     out = {k: host(v) for k, v in g.items()}
     out["y"] = host(y)
@@ -82,15 +86,16 @@ def test_kept_activations(M, name):
     say(f"[train] {name} T={w.T} d={w.d} F={w.F} E={w.E} K={w.K} packed={c['packed']}")
     W = mi.layer_weights(w)
     x = mi.tokens(w)
-    kept = run(M, w, W, x, c["packed"], keep=True)
-    plain = run(M, w, W, x, c["packed"], keep=False)
+    bias = (0.5 * np.random.default_rng(w.seed).standard_normal(w.E)).astype(np.float32) if c.get("bias") else None
+    kept = run(M, w, W, x, c["packed"], keep=True, bias=bias)
+    plain = run(M, w, W, x, c["packed"], keep=False, bias=bias)
     # every routed row's a and b were written (the buffer started as NaN)
     assert np.isfinite(kept["act"]).all()
     for k in ("dx", "dw_gate", "dw1", "dw3", "dw2", "dlogits"):
         assert np.array_equal(kept[k], plain[k]), k
     if c["tiled"]:
         assert np.array_equal(kept["y"], plain["y"])
-    r = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K)
+    r = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, bias=bias)
     keep = gaps(r["logits"], w.K)[0] > TIE
     assert keep.mean() > 0.99
     err = rel_err(kept["y"][keep], r["y"][keep])
