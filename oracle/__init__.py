@@ -38,8 +38,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
+        build()  # compiles only when the library is missing or older than oracle.cpp
         L = ctypes.CDLL(_LIB)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         L.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]
@@ -48,7 +47,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp, i32]
         L.oracle_combine.argtypes = [i64, vp, i32, i32, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
-                                     vp, i32]
+                                     vp, vp, i32]
         L.oracle_rmsnorm_bf16.argtypes = [i64, i32, dbl, vp, vp, vp]
         L.oracle_deep_layer.argtypes = [i64, i32, i32, i32, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_forward_exact.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp]
@@ -61,7 +60,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_rope.argtypes = [i64, i32, i32, dbl, i64, i32, vp, vp]
         L.oracle_attention.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, i32]
         L.oracle_block.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, dbl, dbl, i32, vp, vp, vp, vp, vp, vp,
-                                   vp, vp, i64, vp, vp, vp, vp, vp, vp, i32]
+                                   vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_abi_version.restype = i32
+        assert L.oracle_abi_version() == 2, "liboracle.so is out of date: rebuild it (oracle.build(force=True))"
         _lib = L
     return _lib
 
@@ -148,8 +149,23 @@ def combine(y_perm, token_row, topk_w, tokens=None):
     return y
 
 
-def forward(x, w_gate, w1, w3, w2, K, bias=None, tokens=None, threads=0):
-    """Full layer on selected tokens. Returns dict(y, logits, idx, w) for those tokens."""
+def _selection(select, n, K, E):
+    """A selection override: [n][K] distinct expert ids per row, in slot order (None: TopK's own)."""
+    if select is None:
+        return None
+    s = _c(np.asarray(select).reshape(n, K), np.int32)
+    assert ((s >= 0) & (s < E)).all(), "expert ids out of range"
+    assert all(len(set(r)) == K for r in s.tolist()), "the K experts of a token must be distinct"
+    return s
+
+
+def forward(x, w_gate, w1, w3, w2, K, bias=None, tokens=None, threads=0, select=None):
+    """Full layer on selected tokens. Returns dict(y, logits, idx, w) for those tokens.
+
+    select [n][K] (optional): the experts each selected token keeps, in slot order, instead of the
+    TopK by argmax; for tokens whose TopK is not unique (kept and dropped logits equal within the
+    decision precision), so that the layer can be evaluated under another valid selection. The gates
+    are then the softmax over the logits of the given experts."""
     x, w_gate, w1, w3, w2 = _c(x), _c(w_gate), _c(w1), _c(w3), _c(w2)
     bias = _c(bias, np.float32)
     T, d = x.shape
@@ -157,12 +173,13 @@ def forward(x, w_gate, w1, w3, w2, K, bias=None, tokens=None, threads=0):
     dt = _dtype_code(x)
     tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
     n = tokens.shape[0]
+    sel = _selection(select, n, K, E)
     y = np.empty((n, d), np.float64)
     logits = np.empty((n, E), np.float64)
     idx = np.empty((n, K), np.int32)
     w = np.empty((n, K), np.float64)
     lib().oracle_forward(T, d, F, E, K, dt, _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n, _p(tokens),
-                         _p(y), _p(logits), _p(idx), _p(w), threads)
+                         _p(sel), _p(y), _p(logits), _p(idx), _p(w), threads)
     return {"y": y, "logits": logits, "idx": idx, "w": w}
 
 
@@ -284,9 +301,11 @@ def attention(q, k, v, Hq, Hkv, tokens=None, threads=0):
     return out
 
 
-def block(h, w_qkv, w_o, w_gate, w1, w3, w2, K, Hq, Hkv, base, eps, tokens=None, bias=None, threads=0):
+def block(h, w_qkv, w_o, w_gate, w1, w3, w2, K, Hq, Hkv, base, eps, tokens=None, bias=None, threads=0,
+          select=None):
     """One decoder block of a single sequence. h [T][d] float64 (residual stream in), weights as
     bf16 bit patterns: w_qkv [(Hq+2Hkv)*D][d], w_o [d][Hq*D], MoE weights as in forward().
+    select: a selection override for the MoE sub-block of the selected tokens, as in forward().
     Returns dict(h1, x2, h2, idx, logits) for the selected tokens."""
     h = _c(h, np.float64)
     w_qkv, w_o, w_gate, w1, w3, w2 = _c(w_qkv), _c(w_o), _c(w_gate), _c(w1), _c(w3), _c(w2)
@@ -299,9 +318,11 @@ def block(h, w_qkv, w_o, w_gate, w1, w3, w2, K, Hq, Hkv, base, eps, tokens=None,
     assert w_qkv.shape == ((Hq + 2 * Hkv) * D, d) and w_o.shape == (d, Hq * D) and Hq % Hkv == 0
     tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
     n = tokens.shape[0]
+    sel = _selection(select, n, K, E)
     out = {"h1": np.empty((n, d)), "x2": np.empty((n, d), np.uint16), "h2": np.empty((n, d)),
            "idx": np.empty((n, K), np.int32), "logits": np.empty((n, E))}
     lib().oracle_block(T, d, Hq, Hkv, D, F, E, K, float(base), float(eps), 1, _p(h), _p(w_qkv), _p(w_o),
-                       _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n, _p(tokens), _p(out["h1"]), _p(out["x2"]),
+                       _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), n, _p(tokens), _p(sel), _p(out["h1"]),
+                       _p(out["x2"]),
                        _p(out["h2"]), _p(out["idx"]), _p(out["logits"]), threads)
     return out

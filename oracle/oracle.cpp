@@ -29,7 +29,16 @@
  *     GPU kernel decides in; the sums themselves are exact-order double;
  *   - rows of one expert group are ordered by ascending token index;
  *   - the deep-stack layer is h <- h + MoE(bf16(h / sqrt(mean(h^2) + eps)))
- *     with a unit norm weight (the pages do not describe a norm).
+ *     with a unit norm weight (the pages do not describe a norm);
+ *   - TopK keeps "the K largest values" (csdn blog section 2.2), which names no
+ *     single answer when kept and dropped logits are equal within the precision
+ *     the decision is taken in. Any K experts whose logits are all at least as
+ *     large as every dropped one then satisfy the definition. For those tokens
+ *     the forward and block entry points accept a selection override: the given
+ *     K experts, in the given slot order, replace the argmax choice, and the
+ *     gates are the softmax over their logits, exactly as for a chosen set. The
+ *     rest of the computation is unchanged, so passing the oracle's own
+ *     selection reproduces its result bit for bit.
  *
  * Storage types of inputs: dtype 0 = fp32, dtype 1 = bf16 bit patterns, dtype 2 =
  * fp64 (used by the finite-difference checks of the backward pass). A bf16 value
@@ -118,9 +127,12 @@ void parallel_for(int64_t n, int threads, F body) {
 
 // Router for one token: logits, TopK by repeated argmax on the fp32-rounded logits, softmax of
 // the kept ones. round_logits: the returned logits (and so the gates) are the fp32-rounded values
-// (forward) or the unrounded double sums (backward and its finite-difference checks).
+// (forward) or the unrounded double sums (backward and its finite-difference checks). forced
+// (nullable, K distinct expert ids): the selection to keep instead of the argmax choice, in slot
+// order (the override for tokens whose TopK is not unique; see the header).
 void route_token(int d, int E, int K, int dtype, const void* x, int64_t t, const void* w_gate,
-                 const float* bias, double* logits, int32_t* idx, double* w, bool round_logits = true) {
+                 const float* bias, double* logits, int32_t* idx, double* w, bool round_logits = true,
+                 const int32_t* forced = nullptr) {
   std::vector<double> decide(E);
   for (int e = 0; e < E; ++e) {
     double s = 0.0;
@@ -132,8 +144,12 @@ void route_token(int d, int E, int K, int dtype, const void* x, int64_t t, const
   std::vector<char> taken(E, 0);
   for (int j = 0; j < K; ++j) {
     int best = -1;
-    for (int e = 0; e < E; ++e)
-      if (!taken[e] && (best < 0 || decide[e] > decide[best])) best = e;
+    if (forced) {
+      best = forced[j];
+    } else {
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || decide[e] > decide[best])) best = e;
+    }
     taken[best] = 1;
     idx[j] = best;
   }
@@ -254,7 +270,7 @@ void token_backward(int d, int F, int E, int K, int dtype, const void* x, int64_
 
 extern "C" {
 
-int oracle_abi_version() { return 1; }
+int oracle_abi_version() { return 2; }
 
 // logits [T][E] (double holding fp32-rounded values), topk_idx [T][K], topk_w [T][K].
 void oracle_route(int64_t T, int d, int E, int K, int dtype, const void* x, const void* w_gate,
@@ -319,13 +335,15 @@ void oracle_combine(int64_t n_sel, const int64_t* tok_sel, int d, int K, const f
 
 // Whole layer for selected tokens (tokens are independent): y_sel [n_sel][d];
 // also returns each selected token's logits [n_sel][E], topk_idx [n_sel][K], topk_w [n_sel][K].
+// sel_in [n_sel][K] (nullable): a selection override per selected token (see the header).
 void oracle_forward(int64_t T, int d, int F, int E, int K, int dtype, const void* x, const void* w_gate,
                     const float* bias, const void* w1, const void* w3, const void* w2, int64_t n_sel,
-                    const int64_t* tok_sel, double* y_sel, double* logits_sel, int32_t* idx_sel,
-                    double* w_sel, int threads) {
+                    const int64_t* tok_sel, const int32_t* sel_in, double* y_sel, double* logits_sel,
+                    int32_t* idx_sel, double* w_sel, int threads) {
   (void)T;
   for (int64_t i = 0; i < n_sel; ++i)
-    route_token(d, E, K, dtype, x, tok_sel[i], w_gate, bias, logits_sel + i * E, idx_sel + i * K, w_sel + i * K);
+    route_token(d, E, K, dtype, x, tok_sel[i], w_gate, bias, logits_sel + i * E, idx_sel + i * K, w_sel + i * K,
+                true, sel_in ? sel_in + i * K : nullptr);
   std::vector<double> outs((size_t)n_sel * K * d);
   parallel_for(n_sel * K, threads, [&](int64_t u) {
     int64_t i = u / K;
@@ -366,8 +384,8 @@ void oracle_deep_layer(int64_t n, int d, int F, int E, int K, double eps, double
   std::vector<int64_t> sel(n);
   for (int64_t i = 0; i < n; ++i) sel[i] = i;
   std::vector<double> y((size_t)n * d), w((size_t)n * K);
-  oracle_forward(n, d, F, E, K, 1, x.data(), w_gate, bias, w1, w3, w2, n, sel.data(), y.data(), logits_out,
-                 idx_out, w.data(), threads);
+  oracle_forward(n, d, F, E, K, 1, x.data(), w_gate, bias, w1, w3, w2, n, sel.data(), nullptr, y.data(),
+                 logits_out, idx_out, w.data(), threads);
   for (size_t i = 0; i < (size_t)n * d; ++i) h[i] += y[i];
 }
 
@@ -517,10 +535,12 @@ void oracle_attention(int64_t T, int Hq, int Hkv, int D, int dtype, const void* 
 // tokens h1 [n_sel][d] (after attention), x2 [n_sel][d] (bf16 bits of the MoE input) and
 // h2 [n_sel][d] (after the MoE), plus the routing of x2 (idx [n_sel][K], logits [n_sel][E]).
 // Rows 0..max(tok_sel) are projected to keys and values, as causal attention needs them.
+// sel_in [n_sel][K] (nullable): a selection override for the MoE sub-block (see the header).
 void oracle_block(int64_t T, int d, int Hq, int Hkv, int D, int F, int E, int K, double base, double eps,
                   int dtype, const double* h, const void* w_qkv, const void* w_o, const void* w_gate,
                   const float* bias, const void* w1, const void* w3, const void* w2, int64_t n_sel,
-                  const int64_t* tok_sel, double* h1_sel, uint16_t* x2_sel, double* h2_sel, int32_t* idx_sel,
+                  const int64_t* tok_sel, const int32_t* sel_in, double* h1_sel, uint16_t* x2_sel, double* h2_sel,
+                  int32_t* idx_sel,
                   double* logits_sel, int threads) {
   (void)T;
   int64_t n = 0;  // rows needed: 0..max selected position
@@ -583,8 +603,8 @@ void oracle_block(int64_t T, int d, int Hq, int Hkv, int D, int F, int E, int K,
   std::vector<int64_t> all(n_sel);
   for (int64_t i = 0; i < n_sel; ++i) all[i] = i;
   std::vector<double> y((size_t)n_sel * d), w((size_t)n_sel * K);
-  oracle_forward(n_sel, d, F, E, K, 1, x2_sel, w_gate, bias, w1, w3, w2, n_sel, all.data(), y.data(), logits_sel,
-                 idx_sel, w.data(), threads);
+  oracle_forward(n_sel, d, F, E, K, 1, x2_sel, w_gate, bias, w1, w3, w2, n_sel, all.data(), sel_in, y.data(),
+                 logits_sel, idx_sel, w.data(), threads);
   for (int64_t i = 0; i < n_sel * d; ++i) h2_sel[i] = h1_sel[i] + y[i];
 }
 

@@ -315,3 +315,77 @@ def test_generator_is_counter_based():
     assert not np.array_equal(a, mi.normal(mi.key(7, 4, 2), (1000,), 1.0, "bf16"))
     f = mi.normal(mi.key(7, 3, 3), (200000,), 1.0, "f32")
     assert abs(f.mean()) < 0.01 and abs(f.std() - 1.0) < 0.01
+
+
+# ---------------------------------------------------------------- selection override (ties in TopK)
+# TopK keeps "the K largest values" (csdn section 2.2); where kept and dropped logits are equal within
+# the decision precision more than one selection satisfies it, and the layer's output under each is
+# a correct result. The oracle then evaluates the layer under a given selection.
+
+def _masked_bruteforce(x, W, sel, bias=None):
+    """Every expert for every token, then a dense gating vector that is the softmax over the logits of
+    the given experts and exactly 0 elsewhere (csdn sections 1, 2.3 and 2.4)."""
+    X = f64(x)
+    E = W["w1"].shape[0]
+    l = X @ f64(W["w_gate"])
+    if bias is not None:
+        l = l + bias.astype(np.float64)
+    l = l.astype(np.float32).astype(np.float64)
+    masked = np.full_like(l, -np.inf)
+    np.put_along_axis(masked, sel.astype(np.int64), np.take_along_axis(l, sel.astype(np.int64), 1), 1)
+    G = np.exp(masked - masked.max(1, keepdims=True))
+    G /= G.sum(1, keepdims=True)
+    y = np.zeros_like(X)
+    for e in range(E):
+        out = (silu_np(X @ f64(W["w1"][e]).T) * (X @ f64(W["w3"][e]).T)) @ f64(W["w2"][e]).T
+        y += G[:, e:e + 1] * out
+    return y, G
+
+
+@pytest.mark.parametrize("dtype,bias,E,K", [("f32", False, 8, 2), ("bf16", True, 8, 2), ("bf16", False, 16, 3),
+                                            ("f32", True, 8, 1)])
+def test_own_selection_reproduces_forward_bit_for_bit(dtype, bias, E, K):
+    w = mi.Workload("sel_own", T=70, d=64, F=96, E=E, K=K, dtype=dtype, skew_bias=bias, seed=1301)
+    x, W = mi.tokens(w), mi.layer_weights(w)
+    tok = np.array([0, 3, 17, 69], np.int64)
+    r = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], K, bias=W["bias"], tokens=tok)
+    s = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], K, bias=W["bias"], tokens=tok, select=r["idx"])
+    for k in ("y", "logits", "idx", "w"):
+        assert np.array_equal(r[k], s[k]), k
+
+
+@pytest.mark.parametrize("dtype,bias,E,K", [("f32", False, 8, 2), ("bf16", True, 8, 2), ("bf16", False, 16, 3)])
+def test_forced_selection_equals_masked_bruteforce(dtype, bias, E, K):
+    """A selection other than the TopK (the experts ranked 2..K+1, slots in reverse order) equals the
+    dense compute-all-experts brute force gated by the softmax over that selection."""
+    w = mi.Workload("sel_forced", T=50, d=64, F=128, E=E, K=K, dtype=dtype, skew_bias=bias, seed=1302)
+    x, W = mi.tokens(w), mi.layer_weights(w)
+    own = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], K, bias=W["bias"])
+    order = np.argsort(-own["logits"], axis=1, kind="stable")
+    sel = order[:, 1:K + 1][:, ::-1].astype(np.int32)          # not the TopK set, not in logit order
+    r = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], K, bias=W["bias"], select=sel)
+    assert np.array_equal(r["idx"], sel)
+    y, G = _masked_bruteforce(x, W, sel, W["bias"])
+    assert np.abs(r["y"] - y).max() <= 1e-12 * np.abs(y).max()
+    assert np.allclose(np.take_along_axis(G, sel.astype(np.int64), 1), r["w"], rtol=0, atol=1e-15)
+    assert np.allclose(r["w"].sum(1), 1.0, rtol=0, atol=1e-15)
+    assert not np.allclose(r["y"], own["y"])                    # the override changes the result
+
+
+def test_exact_tie_either_selection():
+    """Two experts with identical router columns tie exactly: the oracle keeps the lower index (the
+    tie reading), and the output under the other selection is that of the same layer with the two
+    experts' weights swapped."""
+    w = mi.Workload("sel_tie", T=30, d=64, F=64, E=4, K=1, dtype="f32", seed=1303)
+    x, W = mi.tokens(w), mi.layer_weights(w)
+    W["w_gate"][:, 1] += 10.0 / 64                              # experts 1 and 2 lead for most tokens
+    W["w_gate"][:, 2] = W["w_gate"][:, 1]
+    r = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], 1)
+    tied = np.flatnonzero(r["logits"][:, 1] == r["logits"].max(1))
+    assert len(tied) > 0 and np.all(r["idx"][tied, 0] == 1)
+    alt = r["idx"].copy()
+    alt[tied, 0] = 2
+    a = oracle.forward(x, W["w_gate"], W["w1"], W["w3"], W["w2"], 1, select=alt)
+    sw = [0, 2, 1, 3]
+    b = oracle.forward(x, W["w_gate"], W["w1"][sw], W["w3"][sw], W["w2"][sw], 1)
+    assert np.array_equal(a["y"][tied], b["y"][tied])

@@ -156,3 +156,24 @@ def test_block_attention_half_matches_torch_composition():
                         tokens=sel)
     for key in ("h1", "x2", "h2", "idx"):
         assert np.array_equal(part[key], got[key][sel]), key
+
+
+def test_block_selection_override():
+    """The MoE sub-block under a selection override: the block's own selection reproduces it bit for
+    bit; another selection changes h2 by exactly the layer's difference under the two selections
+    (evaluated by the layer oracle on the block's own x2)."""
+    T, d, Hq, Hkv, D, F, E, K = 9, 32, 4, 2, 8, 16, 4, 2
+    base, eps = 1e6, 1e-5
+    W = block_weights(8, d, Hq, Hkv, D, F, E)
+    h = np.random.default_rng(9).standard_normal((T, d))
+    args = (W["w_qkv"], W["w_o"], W["w_gate"], W["w1"], W["w3"], W["w2"], K, Hq, Hkv, base, eps)
+    got = oracle.block(h, *args)
+    same = oracle.block(h, *args, select=got["idx"])
+    for key in ("h1", "x2", "h2", "idx", "logits"):
+        assert np.array_equal(same[key], got[key]), key
+    alt = np.argsort(-got["logits"], axis=1, kind="stable")[:, 1:K + 1].astype(np.int32)
+    other = oracle.block(h, *args, select=alt)
+    assert np.array_equal(other["x2"], got["x2"]) and np.array_equal(other["idx"], alt)
+    y_own = oracle.forward(got["x2"], W["w_gate"], W["w1"], W["w3"], W["w2"], K)["y"]
+    y_alt = oracle.forward(got["x2"], W["w_gate"], W["w1"], W["w3"], W["w2"], K, select=alt)["y"]
+    assert np.allclose(other["h2"] - got["h2"], y_alt - y_own, rtol=0, atol=1e-12)
