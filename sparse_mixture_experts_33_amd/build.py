@@ -5,6 +5,7 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -26,15 +27,20 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
-    objs = []
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
-    for src in sources():
-        obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
+    srcs = sources()
+    objs = [os.path.join(HERE, "_build", os.path.basename(src) + ".o") for src in srcs]
+
+    def compile_one(src_obj):
+        src, obj = src_obj
         cmd = [HIPCC, *[f for f in FLAGS if f != "-shared"], "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
-        objs.append(obj)
+
+    # one hipcc per source file, a few at a time (each takes a few hundred MB of memory)
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as pool:
+        list(pool.map(compile_one, zip(srcs, objs)))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

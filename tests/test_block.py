@@ -2,10 +2,17 @@
 
 Bars: max|d| / max|ref| <= 2e-2 (the bf16 bar of the layer) for the attention output and for the
 block's update of the residual stream (h_out - h_in). Expected errors are ~5e-3: q, k, v, the
-attention weights and o are rounded to bf16 on the GPU, the oracle keeps double. Tokens whose
-MoE routing has a near-tie between the K-th and (K+1)-th logits are left out of the block
-comparison (a rounding difference upstream may pick the other expert; both are correct).
+attention weights and o are rounded to bf16 on the GPU, the oracle keeps double.
+
+The MoE input of the block (bf16(rmsnorm(h1))) differs between the GPU and the oracle by the bf16
+roundings of the attention sub-block, which moves logits by up to ~3e-3, so the routing bar for
+the block is TIE = 1e-2 rather than the layer's 1e-4. Tokens inside that band are checked under
+each valid selection: TopK keeps the K largest logits (blog.csdn.net explainer, section 2.2), so
+every K-subset whose logits are all within the band of every dropped one is a correct result,
+and the GPU's output must equal the oracle's block under one of them.
 """
+import itertools
+
 import numpy as np
 import pytest
 
@@ -75,6 +82,22 @@ def test_attention_is_deterministic(M):
     assert np.array_equal(gpu_attention(M, w, A), gpu_attention(M, w, A))
 
 
+def test_attention_full_context_sampled(M):
+    """Mixtral's heads over the full 32k context (T = 32768, the length the block is benchmarked
+    at): hundreds of key tiles per query block, the running-maximum rescale and the three-buffer
+    pipeline over the whole sequence. The oracle checks the first and last positions, both sides
+    of key-tile edges early and late, and a position in the middle."""
+    w = mi.Workload("attn_32k", T=32768, d=4096, F=256, seed=933)
+    say(f"[attention] full context T={w.T} Hq={w.n_heads} Hkv={w.n_kv_heads}")
+    A = mi.attention_inputs(w)
+    got = gpu_attention(M, w, A)
+    sel = np.array([0, 63, 64, 16383, 16384, 32703, 32704, 32766, 32767], dtype=np.int64)
+    ref = oracle.attention(A["q"], A["k"], A["v"], w.n_heads, w.n_kv_heads, tokens=sel)
+    err = rel_err(got[sel], ref)
+    say(f"  {len(sel)} positions: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL
+
+
 def test_attention_mixtral_heads_sampled(M):
     """Mixtral's heads (32 query, 8 key-value, width 128) over 4096 positions; the oracle checks
     sampled positions (first, last, both sides of block edges)."""
@@ -100,23 +123,48 @@ def gpu_block(M, w, h0, BW, W):
     return host(h).astype(np.float64)
 
 
+def valid_selections(logits_row, K, band):
+    """Every K-subset (slots in descending logit order) whose kept logits are all within `band` of
+    every dropped one: the selections TopK allows when logits are known only to within `band`."""
+    E = len(logits_row)
+    out = []
+    for S in itertools.combinations(range(E), K):
+        rest = [e for e in range(E) if e not in S]
+        if not rest or min(logits_row[list(S)]) >= max(logits_row[rest]) - band:
+            out.append(sorted(S, key=lambda e: -logits_row[e]))
+    return out
+
+
 def check_block(M, w, tokens=None):
     h0 = mi.residual0(w)
     BW = mi.block_weights(w)
     W = mi.layer_weights(w)
     got = gpu_block(M, w, h0, BW, W)
     h64 = h0.astype(np.float64)
-    ref = oracle.block(h64, BW["w_qkv"], BW["w_o"], W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, w.n_heads,
-                       w.n_kv_heads, w.rope_base, w.eps, tokens=tokens)
+    args = (BW["w_qkv"], BW["w_o"], W["w_gate"], W["w1"], W["w3"], W["w2"], w.K, w.n_heads, w.n_kv_heads,
+            w.rope_base, w.eps)
+    ref = oracle.block(h64, *args, tokens=tokens)
     toks = np.arange(w.T) if tokens is None else tokens
     keep = gaps(ref["logits"], w.K)[0] > TIE
-    say(f"  {keep.sum()} of {len(toks)} tokens without a routing near-tie")
+    say(f"  {keep.sum()} of {len(toks)} tokens without a routing near-tie at {TIE}")
     assert keep.sum() >= 0.9 * len(toks)
     upd_ref = ref["h2"][keep] - h64[toks][keep]
-    err = np.abs(got[toks][keep] - ref["h2"][keep]).max() / np.abs(upd_ref).max()
+    scale = np.abs(upd_ref).max()
+    err = np.abs(got[toks][keep] - ref["h2"][keep]).max() / scale
     err_att = np.abs(got[toks][keep] - ref["h2"][keep]).max()
     say(f"  block update max|d|/max|ref| = {err:.3e} (max|d| = {err_att:.3e})")
     assert err <= TOL
+    # near-ties: the GPU's block output equals the oracle's under one of the valid selections
+    for i in np.flatnonzero(~keep):
+        t = int(toks[i])
+        cands = valid_selections(ref["logits"][i], w.K, TIE)
+        errs = []
+        for c in cands:
+            r = oracle.block(h64, *args, tokens=np.array([t], np.int64), select=np.array([c], np.int32))
+            errs.append(float(np.abs(got[t] - r["h2"][0]).max() / scale))
+        say(f"  near-tie token {t}: {len(cands)} valid selections, best max|d|/max|ref| = {min(errs):.3e} "
+            f"(selection {cands[int(np.argmin(errs))]})")
+        assert min(errs) <= TOL
 
 
 def test_block_small(M):
