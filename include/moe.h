@@ -31,7 +31,8 @@
  *    Accumulation is fp32 in every case.
  *  - Ownership: the caller allocates and frees every buffer, the workspace
  *    included. The library allocates nothing and keeps no pointer after a call
- *    returns.
+ *    returns. (moe_forward_noalloc, for callers that cannot allocate, uses a
+ *    static per-device scratch array instead of a workspace; see there.)
  *  - Asynchrony: a call only enqueues kernels on `stream` (a hipStream_t passed
  *    as void*, NULL = the default stream) and returns. Outputs are valid once
  *    the stream reaches that point; inputs must stay alive until then. No call
@@ -45,7 +46,8 @@
  *    to the lower expert index, and slot k = 0 holds the largest logit.
  *  - Determinism: no call uses floating-point atomics; the same inputs give
  *    bit-identical outputs on every run.
- *  - Calls on different streams share no state and may run concurrently.
+ *  - Calls on different streams share no state and may run concurrently
+ *    (except moe_forward_noalloc calls on one device, which share its scratch).
  *
  * Supported sizes: 1 <= E <= 64, 1 <= K <= min(E, 8), d and F multiples of 64,
  * d <= 65536, T*K < 2^31. Other valid sizes return MOE_ERR_UNSUPPORTED.
@@ -190,6 +192,24 @@ size_t moe_workspace_bytes(const moe_dims* dims);
 moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
                        const void* w3, const void* w2, void* y, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation). The workspace
+ * moe_forward would take lives in a static device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB), one
+ * copy per device, which the library keeps until the process ends; the call runs on the current
+ * device and allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments as in moe_forward, minus workspace and workspace_bytes.
+ *   Sizes whose moe_workspace_bytes() exceeds the scratch return MOE_ERR_WORKSPACE before anything
+ *   is launched (at d = 4096, F = 14336, E = 8, K = 2 the limit is about 700 tokens: the decode
+ *   batches; larger batches call moe_forward with a workspace).
+ *   Every call on a device shares that device's scratch and leaves its contents behind; nothing in
+ *   it needs to start at zero (every piece is written before it is read). Calls that overlap in time
+ *   on one device (on different streams, or from different host threads without ordering between
+ *   their streams) race on the scratch and give undefined results; calls ordered on one stream are
+ *   safe. Results are bit-identical to moe_forward's. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate,
+                               const void* w1, const void* w3, const void* w2, void* y, void* stream);
 
 /* Backward pass of the layer (moe_forward with accumulate = 0). The pages define the forward
  * only; its gradient follows by the chain rule with the TopK selection held fixed. For token t,

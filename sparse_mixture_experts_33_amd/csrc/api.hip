@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "moe.h"
@@ -229,11 +230,40 @@ moe_status check_opts(const moe_dims& m, const moe_opts* o, int* y_dtype) {
   return MOE_OK;
 }
 
+// Scratch of moe_forward_noalloc: the workspace moe_forward would take from its caller, in a
+// static device array (one copy per device, held until the process ends). Host code never uses
+// the array's name as an address: each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) static uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 const char* moe_status_string(moe_status s) {
   switch (s) {
@@ -430,6 +460,21 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
                       y, s);
   MOE_TRY(disarm());
   return check_launch("moe_forward (combine)");
+}
+
+moe_status moe_forward_noalloc(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate,
+                               const void* w1, const void* w3, const void* w2, void* y, void* stream) {
+  // moe_forward validates everything else; the size limit is checked first, before any HIP call
+  MOE_TRY(check_dims(dims, USE_D | USE_F | USE_EK | USE_DTYPE | USE_LAYOUT));
+  const size_t need = layout(*dims).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: these sizes need %zu bytes of workspace; the static scratch holds %zu "
+                "(call moe_forward with a workspace instead)", need, kScratchBytes);
+  if (dims->T == 0) return moe_forward(dims, opts, x, w_gate, w1, w3, w2, y, nullptr, 0, stream);
+  void* ws = nullptr;
+  MOE_TRY(scratch_of_current_device(&ws));
+  return moe_forward(dims, opts, x, w_gate, w1, w3, w2, y, ws, kScratchBytes, stream);
 }
 
 size_t moe_backward_workspace_bytes(const moe_dims* dims) {

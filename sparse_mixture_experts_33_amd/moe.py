@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 
 # every symbol include/moe.h declares
 SYMBOLS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_workspace_bytes",
-           "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_rmsnorm", "moe_attention",
+           "moe_forward", "moe_forward_noalloc", "moe_backward_workspace_bytes", "moe_backward", "moe_rmsnorm", "moe_attention",
            "moe_block_workspace_bytes", "moe_block_forward", "moe_status_string", "moe_last_error",
            "moe_abi_version")
 
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.argtypes = [P(moe_dims)]
         L.moe_workspace_bytes.restype = sz
         L.moe_forward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_noalloc.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp]
         L.moe_backward_workspace_bytes.argtypes = [P(moe_dims)]
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward.argtypes = [P(moe_dims), P(moe_opts), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -114,7 +115,7 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_pack_weights", "moe_forward",
-                     "moe_backward", "moe_rmsnorm", "moe_attention", "moe_block_forward"):
+                     "moe_forward_noalloc", "moe_backward", "moe_rmsnorm", "moe_attention", "moe_block_forward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -201,6 +202,19 @@ def moe_forward(dims: Dims, x, w_gate, w1, w3, w2, y, workspace, gate_bias=None,
         workspace.numel() * workspace.element_size() if workspace is not None and not isinstance(workspace, int) else 0)
     _check(lib().moe_forward(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
                              _ptr(w2), _ptr(y), _ptr(workspace), nbytes, _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static per-device scratch of moe_forward_noalloc
+
+
+def moe_forward_noalloc(dims: Dims, x, w_gate, w1, w3, w2, y, gate_bias=None, y_dtype=None, accumulate=False,
+                        stream=None, stage_events=None, activations=None):
+    """moe_forward with the library's static per-device scratch as its workspace (include/moe.h):
+    allocates nothing; calls overlapping in time on one device race on the scratch."""
+    o = _opts(gate_bias, y_dtype, accumulate, dims.dtype,
+              None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p).value, activations)
+    _check(lib().moe_forward_noalloc(ctypes.byref(dims.c()), ctypes.byref(o), _ptr(x), _ptr(w_gate), _ptr(w1),
+                                     _ptr(w3), _ptr(w2), _ptr(y), _stream(stream)))
 
 
 def moe_backward_workspace_bytes(dims: Dims) -> int:

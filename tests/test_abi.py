@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
     assert [moe.moe_status_string(i) for i in range(5)] == list(moe.moe.STATUS.values())
 
 
@@ -98,6 +98,20 @@ def test_workspace_checks():
                          None) == 1
     acc = moe_opts(None, 0, 2)
     assert L.moe_combine(ctypes.byref(d), ctypes.byref(acc), FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """moe_forward_noalloc refuses, before any HIP call, sizes whose workspace exceeds the static
+    scratch (64 MiB), and validates its dims like moe_forward."""
+    L = moe.lib()
+    assert moe.moe.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = moe.Dims(4096, 4096, 14336, 8, 2, 1)
+    assert moe.moe_workspace_bytes(big) > moe.moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big.c()), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert "static scratch" in moe.moe_last_error()
+    assert moe.moe_workspace_bytes(moe.Dims(32, 4096, 14336, 8, 2, 1)) <= moe.moe.MOE_NOALLOC_SCRATCH_BYTES
+    bad = moe_dims(32, 4096, 14336, 8, 9, 1)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
 
 
 def test_saved_activations_validation():
