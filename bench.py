@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--workload", default="decode_T32")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="decode workload only: skip the prefill and tiny-layer objects of the default run")
     p.add_argument("--probe", choices=["copy"], help="plain copy of known size (counter calibration)")
     p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "train", "block"], default="forward",
                    help="time moe_forward (default), moe_backward (gradients of the layer) or moe_block_forward "
@@ -94,12 +96,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import moe_inputs as mi
-    import sparse_mixture_experts_33_amd as moe
-    from sparse_mixture_experts_33_amd.moe import MOE_STAGE_EXPERT_UP, stage_event_array
 
     torch.cuda.set_device(0)
     if args.probe == "copy":
@@ -113,6 +112,37 @@ def main():
     if args.pass_ == "block":
         block_bench(args, w)
         return
+    out, ctx = forward_bench(w, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, ctx["x_host"], ctx["host_layer0"], args.cpu_seconds)
+    del ctx
+    if args.workload == "decode_T32" and not args.no_extra:
+        # the other single-layer targets, timed in the same run: the prefill layer (the matrix-core
+        # bound target) and the tiny fp32 layer (latency only)
+        torch.cuda.empty_cache()
+        p, pctx = forward_bench(mi.WORKLOADS["prefill_T4096"], min(args.steps, 20), min(args.warmup, 3))
+        del pctx
+        out["prefill_T4096"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "step_tflops", "step_frac_mfma",
+                                                   "roofline")}
+        out["prefill_T4096"]["steps"] = min(args.steps, 20)
+        torch.cuda.empty_cache()
+        t, tctx = forward_bench(mi.WORKLOADS["tiny_f32"], args.steps, args.warmup)
+        del tctx
+        out["tiny_f32"] = {"value": t["value"], "unit": t["unit"], "ms_per_step": t["ms_per_step"],
+                           "steps": args.steps, "dtype": "f32"}
+    print(json.dumps(out), flush=True)
+
+
+def forward_bench(w, steps, warmup):
+    """One step = one moe_forward over the workload's batch (all layers of a stack), inputs resident
+    in HBM, fragment-packed weights. Returns (the bench record without cpu_baseline, host context)."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_33_amd as moe
+    from sparse_mixture_experts_33_amd.moe import MOE_STAGE_EXPERT_UP, stage_event_array
+
     dt = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     s_x = 2 if w.dtype == "bf16" else 4
@@ -181,8 +211,8 @@ def main():
     # Start and end of the dominant kernel (grouped GEMM 1 + SwiGLU), taken from its own dispatch on
     # the stream it runs on, on every `stride`-th timed step: a timed dispatch costs the step about
     # 8 us of extra latency, so timing every step would slow the decode step by ~2%.
-    stride = max(1, args.steps // 10)
-    sampled = list(range(0, args.steps, stride))
+    stride = max(1, steps // 10)
+    sampled = list(range(0, steps, stride))
     ev = {}
     for i in sampled:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -193,17 +223,17 @@ def main():
     ev_arrays = {i: stage_event_array({2 * MOE_STAGE_EXPERT_UP: a.cuda_event, 2 * MOE_STAGE_EXPERT_UP + 1: b.cuda_event})
                  for i, (a, b) in ev.items()}
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(ev_arrays.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    ms_step = elapsed * 1e3 / args.steps
-    tokens_s = w.T * args.steps / elapsed
+    ms_step = elapsed * 1e3 / steps
+    tokens_s = w.T * steps / elapsed
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
 
     # algorithmic work per step (only routed experts count)
@@ -238,8 +268,8 @@ def main():
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -257,10 +287,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x_host, host_layer0, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out, {"x_host": x_host, "host_layer0": host_layer0, "layers": layers}
 
 
 BWD_METRIC = "MoE-layer backward tokens/s + TFLOP/s vs peak (E=8,K=2,d=4096,F=14336)"
@@ -365,7 +392,7 @@ def backward_bench(args, w, train=False):
         out["backward_ms"] = round(call_ms - fwd_ms, 4)
     if not args.no_cpu_baseline:
         import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = oracle_threads()
         sample = np.linspace(0, w.T - 1, 16).astype(np.int64)
         done, reps, t1 = 0, 0, time.perf_counter()
         while True:
@@ -379,7 +406,8 @@ def backward_bench(args, w, train=False):
             if time.perf_counter() - t1 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, **host_cores(),
+                               "kind": "oracle",
                                "sample": ("forward outputs, " if train else "") +
                                          f"dx and logit gradients of {len(sample)} tokens x {reps} repetitions "
                                          f"({el:.1f}s; the weight-gradient sums are not included)"}
@@ -496,7 +524,7 @@ def block_bench(args, w):
     }
     if not args.no_cpu_baseline:
         import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = oracle_threads()
         # early positions: the oracle projects keys and values of every position up to the last one
         sample = np.array([0, 85, 170, 255], dtype=np.int64)
         h64 = h0_host.astype(np.float64)
@@ -509,10 +537,25 @@ def block_bench(args, w):
             if time.perf_counter() - t1 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, **host_cores(),
+                               "kind": "oracle",
                                "sample": f"block outputs of positions {list(map(int, sample))} (keys and values of "
                                          f"positions 0-255 projected each time) x {reps} repetitions ({el:.1f}s)"}
     print(json.dumps(out), flush=True)
+
+
+def host_cores() -> dict:
+    """The host's logical CPUs (as the OS reports them) and those this process may run on; the oracle
+    uses at most 16 threads (the host share of one GPU)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"host_logical_cpus": os.cpu_count(), "host_cpus_usable": usable}
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, host_cores()["host_cpus_usable"]))
 
 
 def cpu_baseline(w, x_host, W, seconds):
@@ -520,7 +563,7 @@ def cpu_baseline(w, x_host, W, seconds):
     import numpy as np
 
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = oracle_threads()
     sample = np.arange(min(w.T, 32), dtype=np.int64) if w.T <= 32 else np.linspace(0, w.T - 1, 16).astype(np.int64)
     done, t0 = 0, time.perf_counter()
     reps = 0
@@ -535,7 +578,8 @@ def cpu_baseline(w, x_host, W, seconds):
     note = f"{len(sample)} tokens of layer 0 x {reps} repetitions ({el:.1f}s)"
     if w.layers > 1:
         note += "; one layer of the stack, so tokens/s is per layer"
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": note}
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, **host_cores(), "kind": "oracle",
+            "sample": note}
 
 
 if __name__ == "__main__":
