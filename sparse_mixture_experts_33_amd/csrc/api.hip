@@ -266,7 +266,11 @@ extern "C" {
 int32_t moe_abi_version(void) { return 5; }
 
 const char* moe_status_string(moe_status s) {
-  switch (s) {
+  // A C caller may pass any int; reading it as the enum type would be undefined in C++ for values
+  // outside the enumerators' range, so the bits are taken as an int.
+  int v = 0;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
