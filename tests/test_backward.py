@@ -29,9 +29,10 @@ def M():
 
 
 CASES = {
-    # small groups: the recomputed and transposed-weight products run on the streaming kernels
+    # small groups (about 75 rows per expert): every product runs on the LDS-tiled kernels, whose
+    # token blocks past a group's end cost no MFMAs, so mostly partly filled tiles
     "stream_e8": dict(w=mi.Workload("bwd_stream_e8", T=300, d=256, F=512, dtype="bf16", seed=801), bias=None),
-    # large groups: LDS-tiled products
+    # large groups: several full tiles per expert
     "tiled_e4": dict(w=mi.Workload("bwd_tiled_e4", T=700, d=256, F=512, E=4, K=2, dtype="bf16", seed=802), bias=None),
     "e16_k4_bias": dict(w=mi.Workload("bwd_e16_k4", T=130, d=256, F=256, E=16, K=4, dtype="bf16", seed=803),
                         bias="rand"),
