@@ -62,13 +62,39 @@ def copy_probe():
     print(json.dumps({"probe": "copy", "bytes_per_copy": n, "copies": 3}), flush=True)
 
 
+def _code_only(src: str) -> str:
+    """C/C++ source with comments removed and runs of whitespace collapsed (string and character
+    literals kept as written), so that editing a comment leaves the digest of the code unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(files) -> str:
-    """sha256 (first 16 hex digits) of the named kernel sources, in the order given: a counter summary
-    is only valid for the source it was taken on."""
+    """sha256 (first 16 hex digits) of the code of the named kernel sources (comments and layout
+    ignored), in the order given: a counter summary is only valid for the code it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mixture_experts_33_amd", "csrc")
     for f in files:
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

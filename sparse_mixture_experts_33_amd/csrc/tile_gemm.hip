@@ -4,10 +4,11 @@
 //
 //   C[w][t] = sum_k W[w][k] * X[t][k]     (w: weight row = output column, t: token row of the group)
 //
-// Workgroup tile: BW weight rows x BT tokens (SwiGLU: BW/2 rows of w1 and the same BW/2 rows of
-// w3, so that silu(a)*b is formed in registers), 128 KB of LDS stages. Eight wavefronts
-// (two per SIMD, so one's LDS and memory waits overlap the other's MFMAs) in a 2 x 4
-// arrangement, each BW/2 weight rows x BT/4 tokens, 16x16x32 bf16 MFMAs accumulating in fp32.
+// Workgroup tile: BW = 256 weight rows x up to BT token rows (SwiGLU: 128 rows of w1 and the same
+// 128 rows of w3, so that silu(a)*b is formed in registers); BT = 320 for the forward products,
+// 256 for the backward ones. Eight wavefronts (two per SIMD, so one's LDS and memory waits overlap
+// the other's MFMAs) in a 2 x 4 arrangement, each 128 weight rows x BT/4 tokens, 16x16x32 bf16
+// MFMAs accumulating in fp32 (160 accumulator registers per lane at BT = 320).
 //
 // LDS holds both operands in matrix-core fragment order: a fragment is 16 rows x 32 k, 1 KB,
 // lane l holding row l%16 and k = 8*(l/16)..+7. Every global->LDS write and every LDS->register
@@ -19,21 +20,26 @@
 // blocks; the linear index is remapped so that adjacent tiles go to workgroups on the same XCD
 // (workgroups are dealt round-robin over the 8 XCDs), which keeps those blocks in that XCD's L2.
 //
-// Token blocks (16 rows) are dealt to the four token wavefronts round-robin (wavefront t owns
-// blocks t, t+4, t+8, t+12), so the partly filled last tile of a group spreads its rows over the
-// SIMDs; a wavefront skips the MFMAs (and fragment reads) of blocks that lie wholly past the
-// group's end. Token rows past the end still load a valid row and are never stored.
+// A group of n rows takes ceil(n / BT) token tiles and its 16-row blocks are dealt over them as
+// evenly as possible, so no tile holds only a few rows (such a tile would stream a whole slice of
+// the expert's weights for them). Token blocks are dealt to the four token wavefronts round-robin
+// (wavefront t owns blocks t, t+4, ...), so a partly filled tile spreads its rows over the SIMDs;
+// a wavefront skips the MFMAs (and fragment reads) of blocks that lie wholly past the tile's rows.
+// Token rows past the end inside a block load a valid row and are never stored.
 //
 // Forward products (weights [E][N][K], packed or row-major): k-steps of 32 through four LDS stages
-// of 32 KB, filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
-// the destination + 16 l, which is fragment order), so three steps are in flight while one is
-// multiplied and no registers stage the data. Per step s: wait until this wavefront's loads of
-// step s have landed (vmcnt, counting the loads issued after them), barrier (then every
-// wavefront's have), issue step s+3 into the stage that step s-1 used, read the fragments of step
-// s, multiply. The fragment reads are inline assembly that waits for its own results: the
+// of 16 weight and BT/16 token fragments (36 KB at BT = 320), filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the destination + 16 l, which is fragment
+// order), so three steps are in flight while one is multiplied and no registers stage the data. Per
+// step s: wait until this wavefront's loads of step s have landed (vmcnt, counting the loads issued
+// after them), barrier (then every wavefront's have, and every wavefront is done with step s-1),
+// read the fragments of step s, multiply, then issue step s+3 into the stage that step s-1 used.
+// The loads go after the MFMAs because issuing them can hold a wavefront for hundreds of cycles
+// when the vector-memory queue is full; issued last, that wait overlaps the other wavefront's MFMAs
+// on the same SIMD. The fragment reads are inline assembly that waits for its own results: the
 // compiler cannot tell them apart from the asynchronous LDS writes and would otherwise wait for
-// every load in flight before each read; for the same reason the barrier is a bare s_barrier
-// (a workgroup fence makes the compiler drain all loads first).
+// every load in flight before each read; for the same reason the barrier is a bare s_barrier (a
+// workgroup fence makes the compiler drain all loads first).
 //
 // Backward products (WT, WGRAD): k-steps of 64 through two stages staged in registers. Per step s:
 // write step s+1 (loaded during step s-1) to the free stage, load step s+2, multiply step s,
@@ -49,6 +55,7 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kFwdBT = 320;  // token rows per tile of the forward products (at most)
 
 __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 
@@ -148,7 +155,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     out += (int64_t)e * M * N;
   } else {
     while (tile >= s_tile0[e + 1]) ++e;
-    const int mtiles = (s_off[e + 1] - s_off[e] + BT - 1) / BT;
+    const int n_e = s_off[e + 1] - s_off[e];
+    const int mtiles = (n_e + BT - 1) / BT;
+    // the group's rows are dealt over its mtiles token tiles in whole 16-row blocks, as evenly as
+    // possible (q blocks per tile, the last tile the rest), so no tile holds only a few rows
+    const int q = ((n_e + 15) / 16 + mtiles - 1) / mtiles;
     const int local = tile - s_tile0[e];
     // token tiles in bands of 4: within a band the token tile varies fastest, then the weight
     // tile, so the 32 tiles an XCD runs at once cover 4 token x 8 weight tiles even for a group
@@ -157,8 +168,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     const int w = local - band * 4 * NT;
     mt = mb + w % bs;
     nt = w / bs;
-    r0 = s_off[e] + mt * BT;
-    nrows = min(BT, s_off[e + 1] - r0);
+    r0 = s_off[e] + mt * q * 16;
+    nrows = min(q * 16, s_off[e + 1] - r0);
     nsteps_all = K / 64;
   }
   e = __builtin_amdgcn_readfirstlane(e);
@@ -320,18 +331,27 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
   const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
   if constexpr (!WT && !WGRAD) {
-    // forward: k-steps of 32, four stages of 32 KB (16 weight then 16 token fragments), direct loads
-    constexpr int SB = 32768;
-    static_assert(BW == 256 && BT == 256, "stage layout below assumes 256 x 256 tiles");
+    // forward: k-steps of 32, four stages of 16 weight then BT/16 token fragments (1 KB each),
+    // direct loads. Wavefront w loads weight fragments w and w + 8 and the token fragments w + 8i
+    // that exist (BT = 320: 20 of them, so wavefronts 0-3 take three) and hold rows of the group:
+    // fragments wholly past the group's end are not loaded (no wavefront reads them).
+    static_assert(BW == 256 && (BT == 256 || BT == 320), "stage layout below assumes 256 x 256 or 256 x 320");
+    constexpr int TB = BT / 16;                  // token fragments per stage
+    constexpr int SB = (16 + TB) * 1024;         // bytes per stage
+    constexpr int TI = (TB + 7) / 8;             // token fragment slots per wavefront
     typedef __attribute__((address_space(3))) void* lds_ptr;
     const int s0 = s_lo * 2, s1 = s_hi * 2;
-    int32_t trow[2];
+    const int nblk = (nrows + 15) / 16;          // token fragments holding rows of the group
+    int32_t trow[TI];
+    int ntl = 0;                                 // token fragments this wavefront loads per step
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TI; ++i) {
       const int rr = (wave + 8 * i) * 16 + (lane & 15);
       const int r = r0 + (rr < nrows ? rr : 0);
       trow[i] = row_src ? row_src[r] : r;
+      ntl += (wave + 8 * i < TB && wave + 8 * i < nblk) ? 1 : 0;
     }
+    const int nl = 2 + ntl;                      // loads per step (uniform over the wavefront)
     const int wl32 = PACKED ? lane * 8 : (lane & 15) * K + (lane >> 4) * 8;
     constexpr int64_t kW32 = PACKED ? 512 : 32;
     auto dma = [&](int s) {
@@ -350,10 +370,26 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                          (lds_ptr)(base + (wave + 8 * i) * 1024), 16, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
-            (lds_ptr)(base + 16384 + (wave + 8 * i) * 1024), 16, 0, 0);
+      for (int i = 0; i < TI; ++i)
+        if (i < ntl)  // the loaded fragments are the first ntl slots (blocks grow with i)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
+              (lds_ptr)(base + 16384 + (wave + 8 * i) * 1024), 16, 0, 0);
+    };
+    // Wait until at most n loads of this wavefront are in flight (n = a multiple of nl <= 2 * 5).
+    auto wait_vm = [](int n) {
+      switch (n) {
+        case 10: __builtin_amdgcn_s_waitcnt(0xF7A); break;  // vmcnt(10)
+        case 9: __builtin_amdgcn_s_waitcnt(0xF79); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+        default: __builtin_amdgcn_s_waitcnt(0xF70); break;  // vmcnt(0)
+      }
     };
     // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
     // fragment (block wt); the others are at the constant offsets in the reads below
@@ -364,18 +400,12 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       for (int i = 0; i < 3; ++i)
         if (s0 + i < s1) dma(s0 + i);
       for (int s = s0; s < s1; ++s) {
-        const int ahead = min(2, s1 - 1 - s);  // steps issued after s (4 loads each)
-        if (ahead >= 2)
-          __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt(8)
-        else if (ahead == 1)
-          __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4)
-        else
-          __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        const int ahead = min(2, s1 - 1 - s);  // steps issued after s (nl loads each)
+        wait_vm(ahead * nl);
         // a bare barrier: a fence here would make the compiler wait for every load in flight
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (s + 3 < s1) dma(s + 3);
         const uint32_t st = (uint32_t)(s & 3) * SB;
         const uint32_t av = aoff + st, bv = boff + st;
         // a wavefront whose token blocks are all past the group's end (in the last, partly filled
@@ -383,48 +413,51 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         if (decltype(full)::value || nbv > 0) {
           // weight blocks wblock(0..7) (SwiGLU: 4 of w1, then the same 4 of w3, 8 blocks apart) and
           // token blocks wt + 4b; early-clobber outputs, since the reads are in flight together
-          u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3;
-          if constexpr (SWIGLU) {
-            asm volatile(
-                "ds_read_b128 %0, %12 offset:0\n"
-                "ds_read_b128 %1, %12 offset:1024\n"
-                "ds_read_b128 %2, %12 offset:2048\n"
-                "ds_read_b128 %3, %12 offset:3072\n"
-                "ds_read_b128 %4, %12 offset:8192\n"
-                "ds_read_b128 %5, %12 offset:9216\n"
-                "ds_read_b128 %6, %12 offset:10240\n"
-                "ds_read_b128 %7, %12 offset:11264\n"
-                "ds_read_b128 %8, %13 offset:0\n"
-                "ds_read_b128 %9, %13 offset:4096\n"
-                "ds_read_b128 %10, %13 offset:8192\n"
-                "ds_read_b128 %11, %13 offset:12288\n"
-                "s_waitcnt lgkmcnt(0)\n"
-                : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
-                  "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
-                : "v"(av), "v"(bv)
-                : "memory");
+          u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3, B4;
+#define MOE_RD_A(o0, o1, o2, o3, o4, o5, o6, o7)                                   \
+  "ds_read_b128 %[a0], %[av] offset:" #o0 "\n"                                    \
+  "ds_read_b128 %[a1], %[av] offset:" #o1 "\n"                                    \
+  "ds_read_b128 %[a2], %[av] offset:" #o2 "\n"                                    \
+  "ds_read_b128 %[a3], %[av] offset:" #o3 "\n"                                    \
+  "ds_read_b128 %[a4], %[av] offset:" #o4 "\n"                                    \
+  "ds_read_b128 %[a5], %[av] offset:" #o5 "\n"                                    \
+  "ds_read_b128 %[a6], %[av] offset:" #o6 "\n"                                    \
+  "ds_read_b128 %[a7], %[av] offset:" #o7 "\n"
+#define MOE_RD_B4                                                                  \
+  "ds_read_b128 %[b0], %[bv] offset:0\n"                                          \
+  "ds_read_b128 %[b1], %[bv] offset:4096\n"                                       \
+  "ds_read_b128 %[b2], %[bv] offset:8192\n"                                       \
+  "ds_read_b128 %[b3], %[bv] offset:12288\n"
+#define MOE_RD_OUT_A                                                                                  \
+  [a0] "=&v"(A0), [a1] "=&v"(A1), [a2] "=&v"(A2), [a3] "=&v"(A3), [a4] "=&v"(A4), [a5] "=&v"(A5),       \
+      [a6] "=&v"(A6), [a7] "=&v"(A7), [b0] "=&v"(B0), [b1] "=&v"(B1), [b2] "=&v"(B2), [b3] "=&v"(B3)
+#define MOE_RD_IN : [av] "v"(av), [bv] "v"(bv) : "memory"
+          if constexpr (SWIGLU && BB == 5) {
+            asm volatile(MOE_RD_A(0, 1024, 2048, 3072, 8192, 9216, 10240, 11264) MOE_RD_B4
+                         "ds_read_b128 %[b4], %[bv] offset:16384\n"
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_RD_OUT_A, [b4] "=&v"(B4) MOE_RD_IN);
+          } else if constexpr (SWIGLU) {
+            asm volatile(MOE_RD_A(0, 1024, 2048, 3072, 8192, 9216, 10240, 11264) MOE_RD_B4
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_RD_OUT_A MOE_RD_IN);
+          } else if constexpr (BB == 5) {
+            asm volatile(MOE_RD_A(0, 1024, 2048, 3072, 4096, 5120, 6144, 7168) MOE_RD_B4
+                         "ds_read_b128 %[b4], %[bv] offset:16384\n"
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_RD_OUT_A, [b4] "=&v"(B4) MOE_RD_IN);
           } else {
-            asm volatile(
-                "ds_read_b128 %0, %12 offset:0\n"
-                "ds_read_b128 %1, %12 offset:1024\n"
-                "ds_read_b128 %2, %12 offset:2048\n"
-                "ds_read_b128 %3, %12 offset:3072\n"
-                "ds_read_b128 %4, %12 offset:4096\n"
-                "ds_read_b128 %5, %12 offset:5120\n"
-                "ds_read_b128 %6, %12 offset:6144\n"
-                "ds_read_b128 %7, %12 offset:7168\n"
-                "ds_read_b128 %8, %13 offset:0\n"
-                "ds_read_b128 %9, %13 offset:4096\n"
-                "ds_read_b128 %10, %13 offset:8192\n"
-                "ds_read_b128 %11, %13 offset:12288\n"
-                "s_waitcnt lgkmcnt(0)\n"
-                : "=&v"(A0), "=&v"(A1), "=&v"(A2), "=&v"(A3), "=&v"(A4), "=&v"(A5), "=&v"(A6), "=&v"(A7),
-                  "=&v"(B0), "=&v"(B1), "=&v"(B2), "=&v"(B3)
-                : "v"(av), "v"(bv)
-                : "memory");
+            asm volatile(MOE_RD_A(0, 1024, 2048, 3072, 4096, 5120, 6144, 7168) MOE_RD_B4
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_RD_OUT_A MOE_RD_IN);
           }
+#undef MOE_RD_A
+#undef MOE_RD_B4
+#undef MOE_RD_OUT_A
+#undef MOE_RD_IN
+          if constexpr (BB == 4) B4 = B3;  // unused: the MFMAs below take blocks b < BB only
           const u32x4_t A[8] = {A0, A1, A2, A3, A4, A5, A6, A7};
-          const u32x4_t B[4] = {B0, B1, B2, B3};
+          const u32x4_t B[5] = {B0, B1, B2, B3, B4};
 #pragma unroll
           for (int b = 0; b < BB; ++b) {
             if (decltype(full)::value || b < nbv) {
@@ -433,6 +466,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
             }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 3 < s1) dma(s + 3);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (s0 < s1) {
@@ -536,8 +572,8 @@ bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F) {
 
 int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   if (!tile_gemm_applies(dtype, rows, E, d, F)) return 1;
-  // Expected tiles of the down projection (a group of n rows takes n/256 + 1/2 token tiles on
-  // average), spread over 256 CUs in rounds of one tile per CU. A split into ks k-ranges turns
+  // Expected tiles of the down projection (a group of n rows takes ceil(n/320) token tiles),
+  // spread over 256 CUs in rounds of one tile per CU. A split into ks k-ranges turns
   // each round into 1/ks of a round; every extra range costs one more fp32 partial written and
   // read back (8*rows*d bytes at ~6.5 TB/s), expressed in tile times (a 256 x 256 x F tile at
   // ~4 TFLOP/s per CU), plus a fixed 0.2 tile times (the fill and drain of each range's k-loop
@@ -545,7 +581,7 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   // is fastest at 2, the skewed T = 16384 layer at 1, the T = 2048 stack within 0.5% at 2..4).
   // The split depends on the sizes only, so the workspace size does too.
   const double per_e = (double)rows / E;
-  const double tiles = (double)E * (per_e / 256.0 + 0.5) * (d / 256);
+  const double tiles = (double)E * std::ceil(per_e / kFwdBT) * (d / 256);
   const double tile_s = 2.0 * 256 * 256 * (double)F / 4.0e12;
   const double part_s = 8.0 * (double)rows * d / 6.5e12;
   int best = 1;
@@ -573,18 +609,18 @@ void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+    launch_tile<256, kFwdBT, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
   else
-    launch_tile<256, 256, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+    launch_tile<256, kFwdBT, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
 }
 
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s,
                          void* h) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+    launch_tile<256, kFwdBT, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
   else
-    launch_tile<256, 256, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+    launch_tile<256, kFwdBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
 }
 
 void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
@@ -595,11 +631,11 @@ void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, 256, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit, y_part,
-                                             s);
+    launch_tile<256, kFwdBT, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
+                                                y_part, s);
   else
-    launch_tile<256, 256, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit, y_part,
-                                              s);
+    launch_tile<256, kFwdBT, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
+                                                 y_part, s);
 }
 
 }  // namespace moe
