@@ -201,6 +201,8 @@ def forward_bench(w, steps, warmup):
             host_layer0 = W
         else:
             del W
+        if w.layers > 1 and (layer + 1) % 4 == 0:
+            log(f"[bench] {w.name}: {layer + 1} of {w.layers} layers generated ({time.time() - t_gen:.0f}s)")
     x_host = mi.tokens(w)
     x = dev(x_host)
     h0 = dev(mi.residual0(w)) if w.layers > 1 else None
