@@ -5,15 +5,23 @@
 //   C[w][t] = sum_k W[w][k] * X[t][k]     (w: weight row = output column, t: token row of the group)
 //
 // Workgroup tile: BW = 256 weight rows x up to BT token rows (SwiGLU: 128 rows of w1 and the same
-// 128 rows of w3, so that silu(a)*b is formed in registers); BT = 320 for the forward products,
-// 256 for the backward ones. Eight wavefronts (two per SIMD, so one's LDS and memory waits overlap
-// the other's MFMAs) in a 2 x 4 arrangement, each 128 weight rows x BT/4 tokens, 16x16x32 bf16
-// MFMAs accumulating in fp32 (160 accumulator registers per lane at BT = 320).
+// 128 rows of w3, so that silu(a)*b is formed in registers); BT = 320 for the products over token
+// rows (forward, and the backward's products on transposed weights), 256 for the weight gradients.
+// Eight wavefronts (two per SIMD, so one's LDS and memory waits overlap the other's MFMAs) in a
+// 2 x 4 arrangement, each 128 weight rows x BT/4 tokens, 16x16x32 bf16 MFMAs accumulating in fp32
+// (160 accumulator registers per lane at BT = 320).
 //
-// LDS holds both operands in matrix-core fragment order: a fragment is 16 rows x 32 k, 1 KB,
-// lane l holding row l%16 and k = 8*(l/16)..+7. Every global->LDS write and every LDS->register
-// read of a wavefront is then one contiguous 1 KB, free of bank conflicts for any bank count.
-// Weights in the packed layout arrive already in that order (1 KB contiguous global loads).
+// LDS holds the row-major operands in matrix-core fragment order: a fragment is 16 rows x 32 k,
+// 1 KB, lane l holding row l%16 and k = 8*(l/16)..+7. Every global->LDS write and every
+// LDS->register read of a wavefront is then one contiguous 1 KB, free of bank conflicts. Weights in
+// the packed layout arrive already in that order (1 KB contiguous global loads). Operands stored
+// k-major (the backward pass's transposed weights, and both operands of the weight gradients) are
+// staged as they lie, 32 rows of 256 columns per k-step, and each matrix-core operand is assembled
+// by two transposing LDS reads (ds_read_b64_tr_b16: in each group of 16 lanes, lanes 4a..4a+3
+// address the 16 columns of row a, and lane i receives column i of the 4 rows, which is 4
+// consecutive k of output row i). Such a block is 16 slots of two 512-byte rows (rows r and r + 4,
+// r = (j & 3) + 8 (j >> 2) for slot j), 1056 bytes apart: the 16 rows one transposing read touches
+// then lie in 16 different slots, whose 32-byte offsets spread them over all banks.
 //
 // Tiles are numbered expert-major, then in bands of 4 token tiles, then weight tile, then token
 // tile within the band, so that the 32 tiles an XCD runs at once share 4 token and 8 weight row
@@ -27,24 +35,20 @@
 // a wavefront skips the MFMAs (and fragment reads) of blocks that lie wholly past the tile's rows.
 // Token rows past the end inside a block load a valid row and are never stored.
 //
-// Forward products (weights [E][N][K], packed or row-major): k-steps of 32 through four LDS stages
-// of 16 weight and BT/16 token fragments (36 KB at BT = 320), filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at the destination + 16 l, which is fragment
-// order), so three steps are in flight while one is multiplied and no registers stage the data. Per
-// step s: wait until this wavefront's loads of step s have landed (vmcnt, counting the loads issued
-// after them), barrier (then every wavefront's have, and every wavefront is done with step s-1),
-// read the fragments of step s, multiply, then issue step s+3 into the stage that step s-1 used.
-// The loads go after the MFMAs because issuing them can hold a wavefront for hundreds of cycles
-// when the vector-memory queue is full; issued last, that wait overlaps the other wavefront's MFMAs
-// on the same SIMD. The fragment reads are inline assembly that waits for its own results: the
-// compiler cannot tell them apart from the asynchronous LDS writes and would otherwise wait for
-// every load in flight before each read; for the same reason the barrier is a bare s_barrier (a
-// workgroup fence makes the compiler drain all loads first).
-//
-// Backward products (WT, WGRAD): k-steps of 64 through two stages staged in registers. Per step s:
-// write step s+1 (loaded during step s-1) to the free stage, load step s+2, multiply step s,
-// barrier. Writing at the start of the step lets the LDS writes complete under the MFMAs instead
-// of holding every wavefront at the barrier.
+// Every product runs k-steps of 32 through four LDS stages (the weight block, then the token
+// block), filled by direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// the destination + 16 l), so three steps are in flight while one is multiplied and no registers
+// stage the data. Per step s: wait until this wavefront's loads of step s have landed (vmcnt,
+// counting the loads issued after them), barrier (then every wavefront's have, and every wavefront
+// is done with step s-1), read the fragments of step s, multiply, then issue step s+3 into the
+// stage that step s-1 used. The loads go after the MFMAs because issuing them can hold a wavefront
+// for hundreds of cycles when the vector-memory queue is full; issued last, that wait overlaps the
+// other wavefront's MFMAs on the same SIMD. The fragment reads are inline assembly that waits for
+// its own results: the compiler cannot tell them apart from the asynchronous LDS writes and would
+// otherwise wait for every load in flight before each read; for the same reason the barrier is a
+// bare s_barrier (a workgroup fence makes the compiler drain all loads first). The weight
+// gradients run over each group's rows: the last step of a group may be partial, and its rows past
+// the group's end are loaded from valid rows and zeroed in registers before the MFMAs.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -55,25 +59,20 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kFwdBT = 320;  // token rows per tile of the forward products (at most)
+constexpr int kBT = 320;  // token rows per tile (at most) of the products over token rows
 
 __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 
 // WGRAD: weight-gradient mode of the backward pass. Per expert e the product runs over the rows of
 // e's group instead of over a fixed K: out[e][m][n] = sum over the group's rows r of
 // act[r][m] * wa[r][n], with act [rows][.] (row stride K) and wa [rows][.] (row stride ldw) the
-// group-sorted rows as they lie (WGRAD requires WT: both operands k-major, read through transposing
-// LDS reads). A k-step takes 64 rows of the group; rows past its end are zeroed in registers. The
-// group sizes come from `offsets` on the device. Tiles are (expert, n tile, m tile), one 256 x 256
-// output tile each.
+// group-sorted rows as they lie (WGRAD requires WT: both operands k-major). A k-step takes 32 rows
+// of the group; rows past its end are zeroed in registers. The group sizes come from `offsets` on
+// the device. Tiles are (expert, n tile, m tile), one 256 x 256 output tile each.
 //
 // WT: the weight operand is stored transposed, [E][K][N] with the N columns contiguous (the layout
 // in which the backward pass holds w2 and w1, w3 for its products): wa holds k < KA = K/2 and wb
-// the rest when wb is given (KA = K otherwise). A k-step of the weight block is staged in LDS as
-// it lies in memory (64 rows of 256 columns, rows padded by 16 elements), and each matrix-core
-// operand is assembled by two transposing LDS reads (ds_read_b64_tr_b16): in each group of 16
-// lanes, lanes 4a..4a+3 address the 16 columns of row a, and lane i receives column i of the 4
-// rows, which is 4 consecutive k of weight row i.
+// the rest when wb is given (KA = K otherwise).
 template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
@@ -85,21 +84,20 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            bf16_t* __restrict__ hout) {
   static_assert(!WGRAD || (!SWIGLU && !PACKED && WT), "the weight-gradient mode reads both operands k-major");
   static_assert(!WT || (!SWIGLU && !PACKED), "transposed weights: plain product only");
+  static_assert(BW == 256 && (BT == 256 || (BT == 320 && !WGRAD)), "tiles are 256 x 256, or 256 x 320 but for WGRAD");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
-  constexpr int WF = BW / 16 * 2;           // weight fragments per k-step (16-row blocks x 2)
-  constexpr int TF = BT / 16 * 2;           // token fragments per k-step
-  constexpr int NWV = 8;                    // wavefronts: 2 over weight rows x 4 over tokens
-  constexpr int WL = WF / NWV;              // weight fragment loads per wavefront per step
-  constexpr int TL = TF / NWV;              // token fragment loads per wavefront per step
   constexpr int AB = BW / 32;               // weight blocks per wavefront
   constexpr int BB = BT / 64;               // token blocks per wavefront
-  constexpr int WROW = BW + 16;             // WT: LDS row of the weight block (elements, padded)
-  constexpr int WPART = WT ? 64 * WROW * 2 : WF * 1024;  // bytes of the weight block per stage
-  constexpr int TROW = BT + 16;             // WGRAD: LDS row of the token block (elements, padded)
-  constexpr int TPART = WGRAD ? 64 * TROW * 2 : TF * 1024;
-  constexpr int STAGE = WPART + TPART;      // bytes per LDS stage
+  constexpr int TB = BT / 16;               // token fragments per stage (fragment-order tokens)
+  constexpr int TI = (TB + 7) / 8;          // token fragment slots per wavefront
+  // A k-major operand block (WT weights, WGRAD tokens) takes 16 slots of two 512-byte rows, 32
+  // bytes apart beyond 1 KB so that the 16 rows one transposing read touches spread over the banks.
+  constexpr int KSLOT = 1056;
+  constexpr int WPB = WT ? 16 * KSLOT : 16 * 1024;     // bytes of the weight block per stage
+  constexpr int TPB = WGRAD ? 16 * KSLOT : TB * 1024;  // bytes of the token block per stage
+  constexpr int SB = WPB + TPB;                        // bytes per stage
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * SB];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_tile0[kMaxExperts + 1];
 
@@ -184,181 +182,74 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     if (p > 0) out = reinterpret_cast<OutT*>(part + (int64_t)(p - 1) * part_stride);
   }
 
-  // This wavefront loads fragments g = wave + 8*i of each stage: 16-row block (wave>>1) + 4*i at
-  // the fixed k-half (wave & 1). Addresses = scalar (wave-uniform) parts + one lane offset.
-  const int qh = wave & 1, b0 = wave >> 1;
-  // first element of the tile's weights (row-major and packed layouts)
-  const int64_t wrow0 = ((int64_t)e * N + n0) * K;
-  const int w_lane = PACKED ? qh * 512 + lane * 8 : (lane & 15) * K + qh * 32 + (lane >> 4) * 8;
-  int32_t tsrc[TL];
-#pragma unroll
-  for (int i = 0; i < TL; ++i) {
-    const int rr = (b0 + 4 * i) * 16 + (lane & 15);
-    const int r = r0 + (rr < nrows ? rr : 0);
-    tsrc[i] = row_src ? row_src[r] : r;
-  }
-  const int t_lane = qh * 32 + (lane >> 4) * 8;
-  // k advance per step: packed weights move 2 fragments (1024 elements) per 16-row block
-  constexpr int64_t kWStep = PACKED ? 1024 : 64;
-
-  // WT: thread loads 8 consecutive columns nc.. of k rows kr0 + 16*i of the step (coalesced rows)
-  const int kr0 = threadIdx.x / (BW / 8), nc = (threadIdx.x % (BW / 8)) * 8;
-  const int KA = (WT && wb) ? K / 2 : K;
-  u32x4_t wreg[WL], treg[TL];
-  const int kend = WGRAD ? s_off[e + 1] : 0, klast = WGRAD ? s_off[E] - 1 : 0;  // group end, last row
-  auto gload = [&](int s) {
-    if constexpr (WGRAD) {
-      // both operands: rows kcol0 + 64 s + kr of the group, zero past its end (loads clamped in bounds)
-#pragma unroll
-      for (int i = 0; i < WL; ++i) {
-        const int kr = (int)kcol0 + s * 64 + kr0 + (512 / (BW / 8)) * i;
-        const int64_t kc = min(kr, klast);
-        const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
-        const u32x4_t wv = load16_nt(wa + kc * ldw + n0 + nc);
-        const u32x4_t tv = load16(act + kc * K + r0 + nc);
-        wreg[i] = kr < kend ? wv : z;
-        treg[i] = kr < kend ? tv : z;
-      }
-      return;
-    }
-    if constexpr (WT) {
-      const bool second = wb && s * 64 >= KA;  // uniform over the step (KA is a multiple of 64)
-      const bf16_t* w = second ? wb : wa;
-      const int64_t k0 = (int64_t)s * 64 - (second ? KA : 0);
-#pragma unroll
-      for (int i = 0; i < WL; ++i)
-        wreg[i] = load16_nt(w + ((int64_t)e * KA + k0 + kr0 + (512 / (BW / 8)) * i) * ldw + n0 + nc);
-    } else
-#pragma unroll
-    for (int i = 0; i < WL; ++i) {
-      int blk = b0 + 4 * i;
-      const bf16_t* w = wa;
-      if constexpr (SWIGLU) {
-        if (i >= WL / 2) {  // blocks BW/32.. hold w3 (b0 + 4i >= BW/32 exactly when i >= WL/2)
-          w = wb;
-          blk -= BW / 32;
-        }
-      }
-      wreg[i] = load16_nt(w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kWStep + w_lane);
-    }
-#pragma unroll
-    for (int i = 0; i < TL; ++i) treg[i] = load16(act + (int64_t)tsrc[i] * K + kcol0 + (int64_t)s * 64 + t_lane);
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < WL; ++i) {
-      if constexpr (WT)
-        store16(base + ((kr0 + (512 / (BW / 8)) * i) * WROW + nc) * 2, wreg[i]);
-      else
-        store16(base + (wave + 8 * i) * 1024 + lane * 16, wreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < TL; ++i) {
-      if constexpr (WGRAD)
-        store16(base + WPART + ((kr0 + (512 / (BT / 8)) * i) * TROW + nc) * 2, treg[i]);
-      else
-        store16(base + WPART + (wave + 8 * i) * 1024 + lane * 16, treg[i]);
-    }
-  };
-  // Matrix-core operand from a k-major block in LDS (64 rows of `row` elements): 16 columns
-  // blk*16.. at k-half q, lane l gets column l%16 at k = 8(l/16)..+7 (two transposing reads).
-  auto trfrag = [&](const uint8_t* blkbase, int row, int blk, int q) -> u32x4_t {
-    typedef __attribute__((ext_vector_type(4))) short v4s;
-    typedef __attribute__((address_space(3))) v4s* lds_v4s;
-    const int g = lane >> 4, a = (lane >> 2) & 3, c = lane & 3;
-    const uint8_t* p = blkbase + ((q * 32 + 8 * g + a) * row + blk * 16 + 4 * c) * 2;
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * row * 2));
-    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-  };
-  // Weight operand of 16-row block blk at k-half q (16 rows x 32 k, lane l: row l%16, k 8(l/16)..+7).
-  auto wfrag = [&](const uint8_t* base, int blk, int q) -> u32x4_t {
-    if constexpr (WT)
-      return trfrag(base, WROW, blk, q);
-    else
-      return load16(base + (blk * 2 + q) * 1024 + lane * 16);
-  };
-
   f32x4_t acc[AB][BB];
 #pragma unroll
   for (int a = 0; a < AB; ++a)
 #pragma unroll
     for (int b = 0; b < BB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // weight block of the wavefront's a-th A fragment
-  auto wblock = [&](int a) -> int {
-    if constexpr (SWIGLU) return a < AB / 2 ? wr * (AB / 2) + a : BW / 32 + wr * (AB / 2) + (a - AB / 2);
-    else return wr * AB + a;
-  };
-
-  // Token fragment of the wavefront's b-th token block (block wt + 4b) at k-half q.
-  auto tfrag = [&](const uint8_t* base, int b, int q) -> u32x4_t {
-    if constexpr (WGRAD)
-      return trfrag(base + WPART, TROW, wt + 4 * b, q);
-    else
-      return load16(base + WPART + ((wt + 4 * b) * 2 + q) * 1024 + lane * 16);
-  };
-  // Multiply one LDS stage. FULL: all BB token blocks of the wavefront hold rows; otherwise only
-  // the first nbv do (the last, partly filled tile of a group).
-  auto compute = [&](const uint8_t* base, auto full) {
-#pragma unroll 1
-    for (int q = 0; q < 2; ++q) {
-      u32x4_t A[AB];
+  // k-steps of 32 through four LDS stages, each the tile's weight block then its token block,
+  // filled by direct global->LDS loads. Wavefront w issues the loads of fragments / slots w and
+  // w + 8 of the weight block and its share of the token block.
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int n_e = s_off[e + 1] - s_off[e];
+  int s0, s1;
+  if constexpr (WGRAD) {
+    s0 = 0;
+    s1 = (n_e + 31) / 32;  // the group's rows, 32 per step; the last step may be partial
+  } else {
+    s0 = p * nsteps_all / ksplit * 2;  // k-range p of ksplit, split at 64-deep boundaries
+    s1 = (p + 1) * nsteps_all / ksplit * 2;
+  }
+  s0 = __builtin_amdgcn_readfirstlane(s0);
+  s1 = __builtin_amdgcn_readfirstlane(s1);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+  // k-major operands: row R of slot j is R1(j) = (j & 3) + 8 (j >> 2) for lanes 0-31 and R1 + 4 for
+  // lanes 32-63, each lane 8 consecutive columns
+  const int ck = (lane & 31) * 8;
+  int kR[2];
 #pragma unroll
-      for (int a = 0; a < AB; ++a) A[a] = wfrag(base, wblock(a), q);
-      if constexpr (decltype(full)::value) {
-        u32x4_t B[BB];
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + 8 * i;
+    kR[i] = (j & 3) + 8 * (j >> 2) + 4 * (lane >> 5);
+  }
+  // transposing reads of a k-major block: lane (g = l/16, a = (l/4)%4, c = l%4) addresses row
+  // 8g + a (slot a + 4g) and row 8g + a + 4 (512 bytes further), columns 4c..4c+3 of the block
+  const uint32_t ktr = (uint32_t)((((lane >> 2) & 3) + 4 * (lane >> 4)) * KSLOT + 8 * (lane & 3));
+  // fragment-order token operand (forward, WT): fragments wave + 8 i that hold rows of the tile
+  const int nblk = (nrows + 15) / 16;
+  int32_t trow[TI];
+  int ntl = 0;
 #pragma unroll
-        for (int b = 0; b < BB; ++b) B[b] = tfrag(base, b, q);
+  for (int i = 0; i < TI; ++i) {
+    const int rr = (wave + 8 * i) * 16 + (lane & 15);
+    const int r = r0 + (rr < nrows ? rr : 0);
+    trow[i] = WGRAD ? 0 : (row_src ? row_src[r] : r);
+    ntl += (wave + 8 * i < TB && wave + 8 * i < nblk) ? 1 : 0;
+  }
+  const int nl = 2 + (WGRAD ? 2 : ntl);  // loads per step (uniform over the wavefront)
+  const int wl32 = PACKED ? lane * 8 : (lane & 15) * K + (lane >> 4) * 8;
+  constexpr int64_t kW32 = PACKED ? 512 : 32;
+  const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // forward: first element of the tile's weights
+  const int KA = (WT && wb) ? K / 2 : K;             // WT: rows of wa (wb holds the rest)
+  const int klast = s_off[E] - 1;                    // WGRAD: last row of the operands
+  auto dma = [&](int s) {
+    uint8_t* base = smem + (s & 3) * SB;
 #pragma unroll
-        for (int a = 0; a < AB; ++a)
-#pragma unroll
-          for (int b = 0; b < BB; ++b) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + 8 * i;
+      const bf16_t* src;
+      if constexpr (WGRAD) {
+        // rows past the group's end are loaded from valid rows and masked in registers
+        const int64_t kc = min((int)kcol0 + s * 32 + kR[i], klast);
+        src = wa + kc * ldw + n0 + ck;
+      } else if constexpr (WT) {
+        const bool second = wb && s * 32 >= KA;  // uniform over the step (KA is a multiple of 32)
+        const bf16_t* w = second ? wb : wa;
+        const int64_t k = (int64_t)s * 32 - (second ? KA : 0) + kR[i];
+        src = w + ((int64_t)e * KA + k) * ldw + n0 + ck;
       } else {
-#pragma unroll
-        for (int b = 0; b < BB; ++b) {
-          if (b < nbv) {
-            const u32x4_t Bb = tfrag(base, b, q);
-#pragma unroll
-            for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], Bb, acc[a][b]);
-          }
-        }
-      }
-    }
-  };
-
-  const int s_lo = p * nsteps_all / ksplit, s_hi = (p + 1) * nsteps_all / ksplit;
-  if constexpr (!WT && !WGRAD) {
-    // forward: k-steps of 32, four stages of 16 weight then BT/16 token fragments (1 KB each),
-    // direct loads. Wavefront w loads weight fragments w and w + 8 and the token fragments w + 8i
-    // that exist (BT = 320: 20 of them, so wavefronts 0-3 take three) and hold rows of the group:
-    // fragments wholly past the group's end are not loaded (no wavefront reads them).
-    static_assert(BW == 256 && (BT == 256 || BT == 320), "stage layout below assumes 256 x 256 or 256 x 320");
-    constexpr int TB = BT / 16;                  // token fragments per stage
-    constexpr int SB = (16 + TB) * 1024;         // bytes per stage
-    constexpr int TI = (TB + 7) / 8;             // token fragment slots per wavefront
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    const int s0 = s_lo * 2, s1 = s_hi * 2;
-    const int nblk = (nrows + 15) / 16;          // token fragments holding rows of the group
-    int32_t trow[TI];
-    int ntl = 0;                                 // token fragments this wavefront loads per step
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int rr = (wave + 8 * i) * 16 + (lane & 15);
-      const int r = r0 + (rr < nrows ? rr : 0);
-      trow[i] = row_src ? row_src[r] : r;
-      ntl += (wave + 8 * i < TB && wave + 8 * i < nblk) ? 1 : 0;
-    }
-    const int nl = 2 + ntl;                      // loads per step (uniform over the wavefront)
-    const int wl32 = PACKED ? lane * 8 : (lane & 15) * K + (lane >> 4) * 8;
-    constexpr int64_t kW32 = PACKED ? 512 : 32;
-    auto dma = [&](int s) {
-      uint8_t* base = smem + (s & 3) * SB;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int blk = wave + 8 * i;
+        int blk = j;
         const bf16_t* w = wa;
         if constexpr (SWIGLU) {
           if (i == 1) {
@@ -366,53 +257,160 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
             blk -= 8;
           }
         }
-        __builtin_amdgcn_global_load_lds((const void*)(w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kW32 + wl32),
-                                         (lds_ptr)(base + (wave + 8 * i) * 1024), 16, 0, 0);
+        src = w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kW32 + wl32;
       }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + j * (WT ? KSLOT : 1024)), 16, 0, 0);
+    }
+    if constexpr (WGRAD) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t kc = min((int)kcol0 + s * 32 + kR[i], klast);
+        __builtin_amdgcn_global_load_lds((const void*)(act + kc * K + r0 + ck),
+                                         (lds_ptr)(base + WPB + (wave + 8 * i) * KSLOT), 16, 0, 0);
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
         if (i < ntl)  // the loaded fragments are the first ntl slots (blocks grow with i)
           __builtin_amdgcn_global_load_lds(
               (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
-              (lds_ptr)(base + 16384 + (wave + 8 * i) * 1024), 16, 0, 0);
-    };
-    // Wait until at most n loads of this wavefront are in flight (n = a multiple of nl <= 2 * 5).
-    auto wait_vm = [](int n) {
-      switch (n) {
-        case 10: __builtin_amdgcn_s_waitcnt(0xF7A); break;  // vmcnt(10)
-        case 9: __builtin_amdgcn_s_waitcnt(0xF79); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
-        default: __builtin_amdgcn_s_waitcnt(0xF70); break;  // vmcnt(0)
-      }
-    };
-    // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
-    // fragment (block wt); the others are at the constant offsets in the reads below
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
-    const uint32_t aoff = lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
-    const uint32_t boff = lds0 + 16384 + wt * 1024 + lane * 16;
-    auto run = [&](auto full) {
-      for (int i = 0; i < 3; ++i)
-        if (s0 + i < s1) dma(s0 + i);
-      for (int s = s0; s < s1; ++s) {
-        const int ahead = min(2, s1 - 1 - s);  // steps issued after s (nl loads each)
-        wait_vm(ahead * nl);
-        // a bare barrier: a fence here would make the compiler wait for every load in flight
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t st = (uint32_t)(s & 3) * SB;
-        const uint32_t av = aoff + st, bv = boff + st;
-        // a wavefront whose token blocks are all past the group's end (in the last, partly filled
-        // tile) skips its fragment reads as well as its MFMAs
-        if (decltype(full)::value || nbv > 0) {
-          // weight blocks wblock(0..7) (SwiGLU: 4 of w1, then the same 4 of w3, 8 blocks apart) and
-          // token blocks wt + 4b; early-clobber outputs, since the reads are in flight together
+              (lds_ptr)(base + WPB + (wave + 8 * i) * 1024), 16, 0, 0);
+    }
+  };
+  // Wait until at most n loads of this wavefront are in flight (n = a multiple of nl <= 2 * 5).
+  auto wait_vm = [](int n) {
+    switch (n) {
+      case 10: __builtin_amdgcn_s_waitcnt(0xF7A); break;  // vmcnt(10)
+      case 9: __builtin_amdgcn_s_waitcnt(0xF79); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+      default: __builtin_amdgcn_s_waitcnt(0xF70); break;  // vmcnt(0)
+    }
+  };
+  // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
+  // fragment (block wt) in stage 0; the others are at the constant offsets in the reads below
+  const uint32_t aoff = WT ? lds0 + ktr + wr * 256 : lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
+  const uint32_t boff = WGRAD ? lds0 + WPB + ktr + wt * 32 : lds0 + WPB + wt * 1024 + lane * 16;
+  auto run = [&](auto full) {
+    for (int i = 0; i < 3; ++i)
+      if (s0 + i < s1) dma(s0 + i);
+    for (int s = s0; s < s1; ++s) {
+      const int ahead = min(2, s1 - 1 - s);  // steps issued after s (nl loads each)
+      wait_vm(ahead * nl);
+      // a bare barrier: a fence here would make the compiler wait for every load in flight
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t st = (uint32_t)(s & 3) * SB;
+      const uint32_t av = aoff + st, bv = boff + st;
+      // a wavefront whose token blocks are all past the tile's rows skips its fragment reads as
+      // well as its MFMAs
+      if (decltype(full)::value || nbv > 0) {
+        // weight blocks wblock(0..7) and token blocks wt + 4b; early-clobber outputs, since the
+        // reads are in flight together
+        u32x4_t A[8], B[5];
+        if constexpr (WT) {
+          // k-major weights: two transposing reads per fragment (rows 8g + a and 8g + a + 4)
+          u32x2_t L0, L1, L2, L3, L4, L5, L6, L7, H0, H1, H2, H3, H4, H5, H6, H7;
+#define MOE_TR_A                                                                                              \
+  "ds_read_b64_tr_b16 %[l0], %[av] offset:0\n"                                                               \
+  "ds_read_b64_tr_b16 %[h0], %[av] offset:512\n"                                                             \
+  "ds_read_b64_tr_b16 %[l1], %[av] offset:32\n"                                                              \
+  "ds_read_b64_tr_b16 %[h1], %[av] offset:544\n"                                                             \
+  "ds_read_b64_tr_b16 %[l2], %[av] offset:64\n"                                                              \
+  "ds_read_b64_tr_b16 %[h2], %[av] offset:576\n"                                                             \
+  "ds_read_b64_tr_b16 %[l3], %[av] offset:96\n"                                                              \
+  "ds_read_b64_tr_b16 %[h3], %[av] offset:608\n"                                                             \
+  "ds_read_b64_tr_b16 %[l4], %[av] offset:128\n"                                                             \
+  "ds_read_b64_tr_b16 %[h4], %[av] offset:640\n"                                                             \
+  "ds_read_b64_tr_b16 %[l5], %[av] offset:160\n"                                                             \
+  "ds_read_b64_tr_b16 %[h5], %[av] offset:672\n"                                                             \
+  "ds_read_b64_tr_b16 %[l6], %[av] offset:192\n"                                                             \
+  "ds_read_b64_tr_b16 %[h6], %[av] offset:704\n"                                                             \
+  "ds_read_b64_tr_b16 %[l7], %[av] offset:224\n"                                                             \
+  "ds_read_b64_tr_b16 %[h7], %[av] offset:736\n"
+#define MOE_TR_OUT_A                                                                                          \
+  [l0] "=&v"(L0), [l1] "=&v"(L1), [l2] "=&v"(L2), [l3] "=&v"(L3), [l4] "=&v"(L4), [l5] "=&v"(L5),            \
+      [l6] "=&v"(L6), [l7] "=&v"(L7), [h0] "=&v"(H0), [h1] "=&v"(H1), [h2] "=&v"(H2), [h3] "=&v"(H3),         \
+      [h4] "=&v"(H4), [h5] "=&v"(H5), [h6] "=&v"(H6), [h7] "=&v"(H7)
+          if constexpr (WGRAD) {
+            // k-major tokens too: blocks wt + 4b at 128-byte steps
+            u32x2_t M0, M1, M2, M3, N0, N1, N2, N3;
+            asm volatile(MOE_TR_A
+                         "ds_read_b64_tr_b16 %[m0], %[bv] offset:0\n"
+                         "ds_read_b64_tr_b16 %[n0], %[bv] offset:512\n"
+                         "ds_read_b64_tr_b16 %[m1], %[bv] offset:128\n"
+                         "ds_read_b64_tr_b16 %[n1], %[bv] offset:640\n"
+                         "ds_read_b64_tr_b16 %[m2], %[bv] offset:256\n"
+                         "ds_read_b64_tr_b16 %[n2], %[bv] offset:768\n"
+                         "ds_read_b64_tr_b16 %[m3], %[bv] offset:384\n"
+                         "ds_read_b64_tr_b16 %[n3], %[bv] offset:896\n"
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_TR_OUT_A, [m0] "=&v"(M0), [m1] "=&v"(M1), [m2] "=&v"(M2), [m3] "=&v"(M3),
+                           [n0] "=&v"(N0), [n1] "=&v"(N1), [n2] "=&v"(N2), [n3] "=&v"(N3)
+                         : [av] "v"(av), [bv] "v"(bv)
+                         : "memory");
+            B[0] = u32x4_t{M0[0], M0[1], N0[0], N0[1]};
+            B[1] = u32x4_t{M1[0], M1[1], N1[0], N1[1]};
+            B[2] = u32x4_t{M2[0], M2[1], N2[0], N2[1]};
+            B[3] = u32x4_t{M3[0], M3[1], N3[0], N3[1]};
+          } else if constexpr (BB == 5) {
+            asm volatile(MOE_TR_A
+                         "ds_read_b128 %[b0], %[bv] offset:0\n"
+                         "ds_read_b128 %[b1], %[bv] offset:4096\n"
+                         "ds_read_b128 %[b2], %[bv] offset:8192\n"
+                         "ds_read_b128 %[b3], %[bv] offset:12288\n"
+                         "ds_read_b128 %[b4], %[bv] offset:16384\n"
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_TR_OUT_A, [b0] "=&v"(B[0]), [b1] "=&v"(B[1]), [b2] "=&v"(B[2]), [b3] "=&v"(B[3]),
+                           [b4] "=&v"(B[4])
+                         : [av] "v"(av), [bv] "v"(bv)
+                         : "memory");
+          } else {
+            asm volatile(MOE_TR_A
+                         "ds_read_b128 %[b0], %[bv] offset:0\n"
+                         "ds_read_b128 %[b1], %[bv] offset:4096\n"
+                         "ds_read_b128 %[b2], %[bv] offset:8192\n"
+                         "ds_read_b128 %[b3], %[bv] offset:12288\n"
+                         "s_waitcnt lgkmcnt(0)\n"
+                         : MOE_TR_OUT_A, [b0] "=&v"(B[0]), [b1] "=&v"(B[1]), [b2] "=&v"(B[2]), [b3] "=&v"(B[3])
+                         : [av] "v"(av), [bv] "v"(bv)
+                         : "memory");
+          }
+#undef MOE_TR_A
+#undef MOE_TR_OUT_A
+          A[0] = u32x4_t{L0[0], L0[1], H0[0], H0[1]};
+          A[1] = u32x4_t{L1[0], L1[1], H1[0], H1[1]};
+          A[2] = u32x4_t{L2[0], L2[1], H2[0], H2[1]};
+          A[3] = u32x4_t{L3[0], L3[1], H3[0], H3[1]};
+          A[4] = u32x4_t{L4[0], L4[1], H4[0], H4[1]};
+          A[5] = u32x4_t{L5[0], L5[1], H5[0], H5[1]};
+          A[6] = u32x4_t{L6[0], L6[1], H6[0], H6[1]};
+          A[7] = u32x4_t{L7[0], L7[1], H7[0], H7[1]};
+          if constexpr (WGRAD) {
+            if ((n_e & 31) && s == s1 - 1) {
+              // last, partial step of the group: zero the k (row) entries past its end in both
+              // operands; lane l holds k = 8(l/16)..+7, two per register
+              const int lim = n_e - s * 32 - 8 * (lane >> 4);
+              uint32_t m[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) m[q] = 2 * q + 1 < lim ? 0xFFFFFFFFu : (2 * q < lim ? 0x0000FFFFu : 0u);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int a = 0; a < 8; ++a) A[a][q] &= m[q];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) B[b][q] &= m[q];
+              }
+            }
+          }
+        } else {
+          // fragment-order weights (SwiGLU: 4 blocks of w1, then the same 4 of w3, 8 blocks apart)
           u32x4_t A0, A1, A2, A3, A4, A5, A6, A7, B0, B1, B2, B3, B4;
 #define MOE_RD_A(o0, o1, o2, o3, o4, o5, o6, o7)                                   \
   "ds_read_b128 %[a0], %[av] offset:" #o0 "\n"                                    \
@@ -456,47 +454,29 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 #undef MOE_RD_OUT_A
 #undef MOE_RD_IN
           if constexpr (BB == 4) B4 = B3;  // unused: the MFMAs below take blocks b < BB only
-          const u32x4_t A[8] = {A0, A1, A2, A3, A4, A5, A6, A7};
-          const u32x4_t B[5] = {B0, B1, B2, B3, B4};
+          A[0] = A0, A[1] = A1, A[2] = A2, A[3] = A3, A[4] = A4, A[5] = A5, A[6] = A6, A[7] = A7;
+          B[0] = B0, B[1] = B1, B[2] = B2, B[3] = B3, B[4] = B4;
+        }
 #pragma unroll
-          for (int b = 0; b < BB; ++b) {
-            if (decltype(full)::value || b < nbv) {
+        for (int b = 0; b < BB; ++b) {
+          if (decltype(full)::value || b < nbv) {
 #pragma unroll
-              for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
-            }
+            for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 3 < s1) dma(s + 3);
-        __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    if (s0 < s1) {
-      if (nbv == BB)
-        run(std::true_type{});
-      else
-        run(std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 3 < s1) dma(s + 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-    auto kloop = [&](auto full) {
-      gload(s_lo);
-      lstore(0);
-      if (s_lo + 1 < s_hi) gload(s_lo + 1);
-      __syncthreads();
-      for (int s = s_lo; s < s_hi; ++s) {
-        const int cur = (s - s_lo) & 1;
-        if (s + 1 < s_hi) lstore(cur ^ 1);
-        if (s + 2 < s_hi) gload(s + 2);
-        if (decltype(full)::value || nbv > 0) compute(smem + cur * STAGE, full);
-        __syncthreads();
-      }
-    };
-    if (s_lo < s_hi) {  // an empty group (WGRAD) leaves the accumulators at zero
-      if (nbv == BB)
-        kloop(std::true_type{});
-      else
-        kloop(std::false_type{});
-    }
+  };
+  if (s0 < s1) {
+    if constexpr (WGRAD)
+      run(std::true_type{});  // the output tile's 256 rows all exist (M is a multiple of 256)
+    else if (nbv == BB)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
@@ -581,7 +561,7 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   // is fastest at 2, the skewed T = 16384 layer at 1, the T = 2048 stack within 0.5% at 2..4).
   // The split depends on the sizes only, so the workspace size does too.
   const double per_e = (double)rows / E;
-  const double tiles = (double)E * std::ceil(per_e / kFwdBT) * (d / 256);
+  const double tiles = (double)E * std::ceil(per_e / kBT) * (d / 256);
   const double tile_s = 2.0 * 256 * 256 * (double)F / 4.0e12;
   const double part_s = 8.0 * (double)rows * d / 6.5e12;
   int best = 1;
@@ -609,32 +589,33 @@ void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, kFwdBT, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+    launch_tile<256, kBT, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
   else
-    launch_tile<256, kFwdBT, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+    launch_tile<256, kBT, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
 }
 
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s,
                          void* h) {
   if (layout == kPacked)
-    launch_tile<256, kFwdBT, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+    launch_tile<256, kBT, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
   else
-    launch_tile<256, kFwdBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+    launch_tile<256, kBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
 }
 
 void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
                     const void* wb, float* out, int ksplit, float* part, hipStream_t s) {
-  launch_tile<256, 256, false, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part, s);
+  launch_tile<256, kBT, false, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part,
+                                                      s);
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t s) {
   if (layout == kPacked)
-    launch_tile<256, kFwdBT, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
+    launch_tile<256, kBT, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
                                                 y_part, s);
   else
-    launch_tile<256, kFwdBT, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
+    launch_tile<256, kBT, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
                                                  y_part, s);
 }
 
