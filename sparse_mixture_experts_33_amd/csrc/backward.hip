@@ -155,28 +155,62 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, 
   }
 }
 
-// dW_g = x^T dlogit in two passes: part[ch][j][e] = sum over the tokens of chunk ch (ascending),
-// then dW_g[j][e] = sum over chunks (ascending). One thread per column j.
-constexpr int kDwgChunk = 128;
-template <int EMAX>
-__global__ __launch_bounds__(256) void dwgate_part_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dlogits,
-                                                          int64_t T, int d, int E, float* __restrict__ part) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+// dW_g partials: chunk c of kDwgChunk tokens, part[c][j][e] = sum over its tokens t (ascending) of
+// x[t][j] * dlogit[t][e]. A thread takes C consecutive columns (8 with up to 8 experts: one 16-byte
+// load per token; 2 beyond) and its token loop is unrolled so that several loads are in flight; the
+// chunks' partials are then added in chunk order by dwgate_sum_kernel.
+constexpr int kDwgChunk = 64;
+template <int EMAX, int C>
+__global__ __launch_bounds__(64) void dwgate_part_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dlogits,
+                                                         int64_t T, int d, int E, float* __restrict__ part) {
+  static_assert(C == 8 || C == 2, "columns per thread");
+  const int j0 = (blockIdx.x * 64 + threadIdx.x) * C;
   const int ch = blockIdx.y;
-  if (j >= d) return;
-  float acc[EMAX];
+  if (j0 >= d) return;
+  float acc[C][EMAX];
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
-  const int64_t t1 = min<int64_t>(T, (int64_t)(ch + 1) * kDwgChunk);
-  for (int64_t t = (int64_t)ch * kDwgChunk; t < t1; ++t) {
-    const float xv = Elem<bf16_t>::to_f32(x[t * d + j]);
+  for (int c = 0; c < C; ++c)
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-      if (e < E) acc[e] = fmaf(xv, dlogits[t * E + e], acc[e]);
+    for (int e = 0; e < EMAX; ++e) acc[c][e] = 0.0f;
+  const int64_t t0 = (int64_t)ch * kDwgChunk, t1 = min<int64_t>(T, t0 + kDwgChunk);
+  constexpr int U = 8;  // tokens whose loads are issued together
+  for (int64_t tb = t0; tb < t1; tb += U) {
+    uint32_t xv[U][C / 2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (C == 8) {
+        const u32x4_t v = tb + u < t1 ? load16(x + (tb + u) * d + j0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[u][q] = v[q];
+      } else {
+        xv[u][0] = tb + u < t1 ? *reinterpret_cast<const uint32_t*>(x + (tb + u) * d + j0) : 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tb + u >= t1) break;
+      const float* dl = dlogits + (tb + u) * E;
+      float xf[C];
+#pragma unroll
+      for (int q = 0; q < C / 2; ++q) {
+        xf[2 * q] = bf16_lo(xv[u][q]);
+        xf[2 * q + 1] = bf16_hi(xv[u][q]);
+      }
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E) {
+          const float g = dl[e];
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[c][e] = fmaf(xf[c], g, acc[c][e]);
+        }
+      }
+    }
   }
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e)
-    if (e < E) part[((int64_t)ch * d + j) * E + e] = acc[e];
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) part[((int64_t)ch * d + j0 + c) * E + e] = acc[c][e];
 }
 
 __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict__ part, int nch, int d, int E,
@@ -225,12 +259,13 @@ void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* t
 
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg, hipStream_t s) {
   const int nch = dwgate_chunks(T);
-  const dim3 g1((unsigned)((d + 255) / 256), (unsigned)nch);
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   if (E <= 8)
-    launch_kernel(dwgate_part_kernel<8>, g1, dim3(256), 0, s, xb, dlogits, T, d, E, part);
+    launch_kernel(dwgate_part_kernel<8, 8>, dim3((unsigned)((d + 511) / 512), (unsigned)nch), dim3(64), 0, s, xb,
+                  dlogits, T, d, E, part);
   else
-    launch_kernel(dwgate_part_kernel<kMaxExperts>, g1, dim3(256), 0, s, xb, dlogits, T, d, E, part);
+    launch_kernel(dwgate_part_kernel<kMaxExperts, 2>, dim3((unsigned)((d + 127) / 128), (unsigned)nch), dim3(64), 0, s,
+                  xb, dlogits, T, d, E, part);
   launch_kernel(dwgate_sum_kernel, dim3((unsigned)(((int64_t)d * E + 255) / 256)), dim3(256), 0, s, part, nch, d, E, dwg);
 }
 
