@@ -97,9 +97,15 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   constexpr int TPB = WGRAD ? 16 * KSLOT : TB * 1024;  // bytes of the token block per stage
   constexpr int SB = WPB + TPB;                        // bytes per stage
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * SB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[WGRAD ? SB : 4 * SB];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_tile0[kMaxExperts + 1];
+  // WGRAD's other three stages are separate arrays, so that in its steady-state loop (below) the
+  // compiler can tell, for a stage named statically, that the direct loads in flight into the other
+  // stages do not write what it reads; the other modes keep the four stages in smem
+  __shared__ __attribute__((aligned(16))) uint8_t stg1[WGRAD ? SB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stg2[WGRAD ? SB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stg3[WGRAD ? SB : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -204,6 +210,14 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   s0 = __builtin_amdgcn_readfirstlane(s0);
   s1 = __builtin_amdgcn_readfirstlane(s1);
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+  auto stage_of = [&](int s) -> uint8_t* {  // stage of step s (WGRAD: s0 = 0)
+    if constexpr (WGRAD) {
+      const int k = s & 3;
+      return k == 0 ? smem : k == 1 ? stg1 : k == 2 ? stg2 : stg3;
+    } else {
+      return smem + (s & 3) * SB;
+    }
+  };
   // k-major operands: row R of slot j is R1(j) = (j & 3) + 8 (j >> 2) for lanes 0-31 and R1 + 4 for
   // lanes 32-63, each lane 8 consecutive columns
   const int ck = (lane & 31) * 8;
@@ -233,8 +247,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // forward: first element of the tile's weights
   const int KA = (WT && wb) ? K / 2 : K;             // WT: rows of wa (wb holds the rest)
   const int klast = s_off[E] - 1;                    // WGRAD: last row of the operands
-  auto dma = [&](int s) {
-    uint8_t* base = smem + (s & 3) * SB;
+  auto dma_to = [&](uint8_t* base, int s) {  // step s into stage `base`
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = wave + 8 * i;
@@ -277,6 +290,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
               (lds_ptr)(base + WPB + (wave + 8 * i) * 1024), 16, 0, 0);
     }
   };
+  auto dma = [&](int s) { dma_to(stage_of(s), s); };
   // Wait until at most n loads of this wavefront are in flight (n = a multiple of nl <= 2 * 5).
   auto wait_vm = [](int n) {
     switch (n) {
@@ -296,17 +310,54 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   // fragment (block wt) in stage 0; the others are at the constant offsets in the reads below
   const uint32_t aoff = WT ? lds0 + ktr + wr * 256 : lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
   const uint32_t boff = WGRAD ? lds0 + WPB + ktr + wt * 32 : lds0 + WPB + wt * 1024 + lane * 16;
-  auto run = [&](auto full) {
-    for (int i = 0; i < 3; ++i)
-      if (s0 + i < s1) dma(s0 + i);
-    for (int s = s0; s < s1; ++s) {
+  // WGRAD steady state: four steps per iteration with the stages named statically and the
+  // transposing fragment reads written as builtins, so that the compiler can schedule the reads of
+  // one step among the MFMAs of the previous one (it overlaps about half of them). Every wavefront
+  // issues 2 + 2 loads per step; runs while step s + 3 exists.
+  auto wgrad_step = [&](auto kc, int s) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    uint8_t* cur = k == 0 ? smem : k == 1 ? stg1 : k == 2 ? stg2 : stg3;
+    uint8_t* nxt = k == 0 ? stg3 : k == 1 ? smem : k == 2 ? stg1 : stg2;  // stage of step s + 3
+    __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt(8): this wavefront's loads of steps <= s landed
+    __builtin_amdgcn_s_barrier();       // ... and every wavefront's
+    asm volatile("" ::: "memory");      // no LDS access moves above the barrier
+    typedef __attribute__((ext_vector_type(4))) short v4s;
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    auto tr = [](const uint8_t* q) __attribute__((always_inline)) -> u32x4_t {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q + 512));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+      return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    };
+    const uint32_t ao = ktr + wr * 256, bo = WPB + ktr + wt * 32;  // this lane's first fragments
+    u32x4_t A[AB], B[BB];
+#pragma unroll
+    for (int a = 0; a < AB; ++a) A[a] = tr(cur + ao + a * 32);
+#pragma unroll
+    for (int b = 0; b < BB; ++b) B[b] = tr(cur + bo + b * 128);
+#pragma unroll
+    for (int b = 0; b < BB; ++b)
+#pragma unroll
+      for (int a = 0; a < AB; ++a) acc[a][b] = mfma_bf16(A[a], B[b], acc[a][b]);
+    asm volatile("" ::: "memory");  // the loads of step s + 3 stay behind this step's reads
+    dma_to(nxt, s + 3);
+  };
+
+  // General steps from s_begin (dynamic stage, wait count and token blocks); from s0 it issues the
+  // first three steps first.
+  auto run = [&](int s_begin, auto full) {
+    if (s_begin == s0)
+      for (int i = 0; i < 3; ++i)
+        if (s0 + i < s1) dma(s0 + i);
+    for (int s = s_begin; s < s1; ++s) {
       const int ahead = min(2, s1 - 1 - s);  // steps issued after s (nl loads each)
       wait_vm(ahead * nl);
       // a bare barrier: a fence here would make the compiler wait for every load in flight
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      const uint32_t st = (uint32_t)(s & 3) * SB;
+      const uint32_t st = WGRAD ? (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)stage_of(s)) - lds0
+                                : (uint32_t)(s & 3) * SB;
       const uint32_t av = aoff + st, bv = boff + st;
       // a wavefront whose token blocks are all past the tile's rows skips its fragment reads as
       // well as its MFMAs
@@ -471,12 +522,28 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     }
   };
   if (s0 < s1) {
-    if constexpr (WGRAD)
-      run(std::true_type{});  // the output tile's 256 rows all exist (M is a multiple of 256)
-    else if (nbv == BB)
-      run(std::true_type{});
-    else
-      run(std::false_type{});
+    if constexpr (WGRAD) {
+      const int s_fast = max(0, (s1 - 3) / 4 * 4);  // steady-state steps (s0 = 0)
+      if (s_fast > 0) {
+        // all three exist here; issued unconditionally (a conditional issue would cost the loop
+        // below a wait for every load at its head)
+        dma_to(smem, 0);
+        dma_to(stg1, 1);
+        dma_to(stg2, 2);
+        for (int s = 0; s < s_fast; s += 4) {
+          wgrad_step(std::integral_constant<int, 0>{}, s);
+          wgrad_step(std::integral_constant<int, 1>{}, s + 1);
+          wgrad_step(std::integral_constant<int, 2>{}, s + 2);
+          wgrad_step(std::integral_constant<int, 3>{}, s + 3);
+        }
+      }
+      run(s_fast, std::true_type{});  // the output tile's 256 rows all exist (M is a multiple of 256)
+    } else {
+      if (nbv == BB)
+        run(s0, std::true_type{});
+      else
+        run(s0, std::false_type{});
+    }
   }
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
