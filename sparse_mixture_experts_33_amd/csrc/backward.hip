@@ -34,22 +34,25 @@ __device__ inline float row_gate(const int32_t* row_token, const int32_t* token_
   return g;
 }
 
-// Per row r = (t, k): dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g_k dy[t]). One block per row.
-__global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict__ dy, const int32_t* __restrict__ row_token,
-                                                        const int32_t* __restrict__ token_row,
+// Per token t and slot k (row r = token_row[t][k], gate g_k): dy_perm[r] = bf16(dy[t]),
+// do_perm[r] = bf16(g_k dy[t]). One block per token, so dy[t] is read once for its K rows.
+__global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict__ dy, const int32_t* __restrict__ token_row,
                                                         const float* __restrict__ topk_w, int K, int d,
                                                         bf16_t* __restrict__ dy_perm, bf16_t* __restrict__ do_perm) {
-  const int r = blockIdx.x;
-  int t;
-  const float g = row_gate(row_token, token_row, topk_w, K, r, t);
+  const int64_t t = blockIdx.x;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dy + (int64_t)t * d + c);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(dy + (int64_t)t * d + c + 4);
-    store16(dy_perm + (int64_t)r * d + c,
-            u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])});
-    store16(do_perm + (int64_t)r * d + c,
-            u32x4_t{pack_bf16x2(g * a[0], g * a[1]), pack_bf16x2(g * a[2], g * a[3]), pack_bf16x2(g * b[0], g * b[1]),
-                    pack_bf16x2(g * b[2], g * b[3])});
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dy + t * d + c);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(dy + t * d + c + 4);
+    const u32x4_t v =
+        u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+    for (int k = 0; k < K; ++k) {
+      const int64_t r = token_row[t * K + k];
+      const float g = topk_w[t * K + k];
+      store16(dy_perm + r * d + c, v);
+      store16(do_perm + r * d + c,
+              u32x4_t{pack_bf16x2(g * a[0], g * a[1]), pack_bf16x2(g * a[2], g * a[3]), pack_bf16x2(g * b[0], g * b[1]),
+                      pack_bf16x2(g * b[2], g * b[3])});
+    }
   }
 }
 
@@ -116,42 +119,58 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 // dx[t] = sum_k dxp[token_row[t][k]] (slot order) + sum_e W_g[:, e] dlogit[t][e] (expert order).
 // When the product that wrote dxp was split into k-ranges, a row of dxp is first rebuilt as the
 // sum of its range partials in range order (part + p*part_stride, p < nparts).
-// One block per token, 4 columns per thread.
+// One block per kDxTokens tokens (the gate weights of a column are read once for all of them),
+// 4 columns per thread.
+constexpr int kDxTokens = 4;
 template <int EMAX>
 __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, const float* __restrict__ part,
                                                  int nparts, int64_t part_stride, const int32_t* __restrict__ token_row,
                                                  const float* __restrict__ dlogits, const bf16_t* __restrict__ w_gate,
-                                                 int d, int E, int K, float* __restrict__ dx) {
-  const int64_t t = blockIdx.x;
-  float dl[EMAX];
+                                                 int64_t T, int d, int E, int K, float* __restrict__ dx) {
+  const int64_t tb = (int64_t)blockIdx.x * kDxTokens;
+  const int nt = (int)min<int64_t>(kDxTokens, T - tb);
+  float dl[kDxTokens][EMAX];
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) dl[e] = e < E ? dlogits[t * E + e] : 0.0f;
-  auto row = [&](int k, int c) {
+  for (int i = 0; i < kDxTokens; ++i)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) dl[i][e] = (i < nt && e < E) ? dlogits[(tb + i) * E + e] : 0.0f;
+  auto row = [&](int64_t t, int k, int c) {
     const int64_t off = (int64_t)token_row[t * K + k] * d + c;
     f32x4_t o = *reinterpret_cast<const f32x4_t*>(dxp + off);
     for (int p = 0; p < nparts; ++p) o = o + *reinterpret_cast<const f32x4_t*>(part + p * part_stride + off);
     return o;
   };
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-    f32x4_t s = row(0, c);
-    for (int k = 1; k < K; ++k) s = s + row(k, c);
+    float wg[4][EMAX];  // W_g[c + q][e]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float rsum = 0.0f;
-      if (EMAX == 8 && E == 8) {
-        // the row's 8 gate weights in one 16-byte load; same order of products as below
-        const u32x4_t wr = load16(w_gate + (int64_t)(c + q) * 8);
+      if constexpr (EMAX == 8) {
+        if (E == 8) {
+          const u32x4_t wr = load16(w_gate + (int64_t)(c + q) * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          rsum = fmaf((e & 1) ? bf16_hi(wr[e >> 1]) : bf16_lo(wr[e >> 1]), dl[e], rsum);
-      } else {
+          for (int e = 0; e < 8; ++e) wg[q][e] = (e & 1) ? bf16_hi(wr[e >> 1]) : bf16_lo(wr[e >> 1]);
+          continue;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) wg[q][e] = e < E ? Elem<bf16_t>::to_f32(w_gate[(int64_t)(c + q) * E + e]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kDxTokens; ++i) {
+      if (i >= nt) break;
+      const int64_t t = tb + i;
+      f32x4_t acc = row(t, 0, c);
+      for (int k = 1; k < K; ++k) acc = acc + row(t, k, c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float rsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < EMAX; ++e)
-          if (e < E) rsum = fmaf(Elem<bf16_t>::to_f32(w_gate[(int64_t)(c + q) * E + e]), dl[e], rsum);
+          if (e < E) rsum = fmaf(wg[q][e], dl[i][e], rsum);
+        acc[q] += rsum;
       }
-      s[q] += rsum;
+      *reinterpret_cast<f32x4_t*>(dx + t * d + c) = acc;
     }
-    *reinterpret_cast<f32x4_t*>(dx + t * d + c) = s;
   }
 }
 
@@ -228,7 +247,8 @@ int dwgate_chunks(int64_t T) { return (int)((T + kDwgChunk - 1) / kDwgChunk); }
 
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
                       int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t s) {
-  launch_kernel(gather_dy_kernel, dim3((unsigned)rows), dim3(256), 0, s, dy, row_token, token_row, topk_w, K, d,
+  (void)row_token;
+  launch_kernel(gather_dy_kernel, dim3((unsigned)(rows / K)), dim3(256), 0, s, dy, token_row, topk_w, K, d,
                 static_cast<bf16_t*>(dy_perm), static_cast<bf16_t*>(do_perm));
 }
 
@@ -250,11 +270,11 @@ void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* t
   const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
   const int64_t stride = T * K * (int64_t)d;
   if (E <= 8)
-    launch_kernel(dx_kernel<8>, dim3((unsigned)T), dim3(256), 0, s, dxp, part, nparts, stride, token_row, dlogits, wg,
-                  d, E, K, dx);
+    launch_kernel(dx_kernel<8>, dim3((unsigned)((T + kDxTokens - 1) / kDxTokens)), dim3(256), 0, s, dxp, part, nparts,
+                  stride, token_row, dlogits, wg, T, d, E, K, dx);
   else
-    launch_kernel(dx_kernel<kMaxExperts>, dim3((unsigned)T), dim3(256), 0, s, dxp, part, nparts, stride, token_row,
-                  dlogits, wg, d, E, K, dx);
+    launch_kernel(dx_kernel<kMaxExperts>, dim3((unsigned)((T + kDxTokens - 1) / kDxTokens)), dim3(256), 0, s, dxp, part,
+                  nparts, stride, token_row, dlogits, wg, T, d, E, K, dx);
 }
 
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg, hipStream_t s) {
