@@ -318,8 +318,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     constexpr int k = decltype(kc)::value;
     uint8_t* cur = k == 0 ? smem : k == 1 ? stg1 : k == 2 ? stg2 : stg3;
     uint8_t* nxt = k == 0 ? stg3 : k == 1 ? smem : k == 2 ? stg1 : stg2;  // stage of step s + 3
-    __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt(8): this wavefront's loads of steps <= s landed
-    __builtin_amdgcn_s_barrier();       // ... and every wavefront's
+    // vmcnt(8) and lgkmcnt(0): this wavefront's loads of steps <= s have landed and its reads of
+    // step s - 1 are complete, so after the barrier every wavefront's are, and the loads issued
+    // into that stage below cannot overtake a read of it
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");      // no LDS access moves above the barrier
     typedef __attribute__((ext_vector_type(4))) short v4s;
     typedef __attribute__((address_space(3))) v4s* lds_v4s;
