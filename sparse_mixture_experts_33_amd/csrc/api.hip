@@ -92,7 +92,8 @@ Workspace layout(const moe_dims& m) {
   w.offsets = o;   o = align256(o + (size_t)(m.E + 1) * 4);
   w.row_token = o; o = align256(o + S * 4);
   w.token_row = o; o = align256(o + S * 4);
-  w.h = o;         o = align256(o + S * (size_t)m.F * elem_bytes(m.dtype));
+  // h: row-major, or fragment-packed with each group padded to 16 rows (tiled path)
+  w.h = o;         o = align256(o + (S + 15 * (size_t)m.E) * (size_t)m.F * elem_bytes(m.dtype));
   w.y_perm = o;    o = align256(o + S * (size_t)m.d * 4);
   w.ksplit = moe::tile_down_ksplit(m.dtype, (int64_t)S, m.E, m.d, m.F);
   w.y_part = o;    o = align256(o + (size_t)(w.ksplit - 1) * S * (size_t)m.d * 4);
@@ -442,21 +443,25 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
   MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (permute)"));
   float* act = opts ? opts->activations : nullptr;
+  // on the tiled path h stays fragment-packed between the two products (both take the same path)
+  const bool hpk = moe::tile_gemm_applies(m.dtype, m.T * m.K, m.E, m.d, m.F);
   if (act) {
     // training: the pre-activations a, b in fp32 (kept for the backward pass) and h, in one product
     float* a = act;
     float* b = act + (size_t)m.T * m.K * m.F;
     arm(MOE_STAGE_EXPERT_UP);
-    moe::launch_tile_up_pair(m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, a, b, s, h);
+    moe::launch_tile_up_pair(m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, a, b, s, h,
+                             hpk);
   } else {
     arm(MOE_STAGE_EXPERT_UP);
-    moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s);
+    moe::launch_expert_up(m.dtype, m.weight_layout, x, row_token, offsets, m.T * m.K, m.d, m.F, m.E, w1, w3, h, s,
+                          hpk);
   }
   MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (expert up)"));
   arm(MOE_STAGE_EXPERT_DOWN);
   moe::launch_expert_down(m.dtype, m.weight_layout, h, offsets, m.T * m.K, m.d, m.F, m.E, w2, y_perm, L.ksplit, y_part,
-                          s);
+                          s, hpk);
   MOE_TRY(disarm());
   MOE_TRY(check_launch("moe_forward (expert down)"));
   arm(MOE_STAGE_COMBINE);

@@ -307,9 +307,10 @@ void launch_stream_l(int layout, const void* act, const int32_t* row_src, const 
 }  // namespace
 
 void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row_src, const int32_t* offsets,
-                      int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream) {
+                      int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream,
+                      bool hpk) {
   if (tile_gemm_applies(dtype, rows, E, d, F))
-    launch_tile_up(layout, act, row_src, offsets, rows, d, F, E, w1, w3, h, stream);
+    launch_tile_up(layout, act, row_src, offsets, rows, d, F, E, w1, w3, h, stream, hpk);
   else if (dtype == kBF16)
     launch_stream_l<bf16_t, true, bf16_t>(layout, act, row_src, offsets, rows, E, w1, w3, h, d, F, stream);
   else
@@ -317,9 +318,10 @@ void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row
 }
 
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
-                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream) {
+                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream,
+                        bool hpk) {
   if (tile_gemm_applies(dtype, rows, E, d, F))
-    launch_tile_down(layout, h, offsets, rows, d, F, E, w2, y_perm, ksplit, y_part, stream);
+    launch_tile_down(layout, h, offsets, rows, d, F, E, w2, y_perm, ksplit, y_part, stream, hpk);
   else if (dtype == kBF16)
     launch_stream_l<bf16_t, false, float>(layout, h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, stream);
   else

@@ -52,12 +52,17 @@ void launch_gather_rows(const void* x, const int32_t* row_token, int64_t rows, i
 // down: y_perm[r] = h[r] . w2[e]^T
 // rows = T*K; the tile shape is chosen from rows/E, and any routing is handled correctly.
 // layout: kRowMajor or kPacked (fragment-packed weights, see moe_pack_weights in moe.h).
+// hpk (tiled path only): h is kept fragment-packed between the two products, each group starting a
+// new 16-row block (tile_gemm.hip, HPK); it then needs (rows + 15 E) x F elements and is read only by
+// launch_expert_down with the same flag. The streaming path ignores it (h row-major).
 void launch_expert_up(int dtype, int layout, const void* act, const int32_t* row_src, const int32_t* offsets,
-                      int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+                      int64_t rows, int d, int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream,
+                      bool hpk = false);
 // ksplit > 1 (moe_forward only, tiled path only): k-range p > 0 writes its partial sums to
 // y_part + (p-1)*rows*d; y_perm then holds only range 0 and the combine adds the rest.
 void launch_expert_down(int dtype, int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F,
-                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
+                        int E, const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream,
+                        bool hpk = false);
 
 // Tiled (LDS-staged, 256 x 256) grouped GEMMs for large groups; tile_gemm_applies says when
 // they are used instead of the streaming kernels.
@@ -65,7 +70,7 @@ bool tile_gemm_applies(int dtype, int64_t rows, int E, int d, int F);
 // k-ranges the down projection of moe_forward is split into (1 = no split).
 int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F);
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
-                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream);
+                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream, bool hpk = false);
 // Grouped product with transposed weights (backward pass): out[r][n] = sum_k act[r][k] W_e[k][n] for the
 // rows r of group e, W_e [K][N] row-major; wa holds k < K/2 and wb the rest when wb is given (wb
 // NULL: wa holds all K). fp32 out, split into ksplit k-ranges as launch_tile_down. N multiple of 256,
@@ -76,9 +81,9 @@ void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N
 // not null, h = bf16(silu(a) b) as the fused product forms it (the forward keeping activations).
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream,
-                         void* h = nullptr);
+                         void* h = nullptr, bool hpk = false);
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
-                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream);
+                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream, bool hpk = false);
 
 // Weight-gradient products of the backward pass (bf16 operands, fp32 out): for each expert e,
 // out[e][m][n] = sum over the rows r of e's group of p[r][m] * q[r][n], p and q group-sorted rows of

@@ -73,7 +73,13 @@ __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 // WT: the weight operand is stored transposed, [E][K][N] with the N columns contiguous (the layout
 // in which the backward pass holds w2 and w1, w3 for its products): wa holds k < KA = K/2 and wb
 // the rest when wb is given (KA = K otherwise).
-template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT>
+// HPK: the hidden activations h between the two forward products are fragment-packed: the up
+// product stores h (and the pair product its h output) and the down product reads it as its token
+// operand in 1 KB fragments of 16 rows x 32 columns (lane l: row l % 16, columns 8 (l / 16)..+7),
+// fragments of a 16-row block consecutive along F. Each group's rows start a new block: row r of
+// group e is packed row hpk_row0(e) + r - offsets[e], hpk_row0(e) = sum over e' < e of the group
+// sizes rounded up to 16 (packed rows past a group's end are never written nor stored from).
+template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT, bool HPK = false>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
                                                            const int32_t* __restrict__ offsets,
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            bf16_t* __restrict__ hout) {
   static_assert(!WGRAD || (!SWIGLU && !PACKED && WT), "the weight-gradient mode reads both operands k-major");
   static_assert(!WT || (!SWIGLU && !PACKED), "transposed weights: plain product only");
+  static_assert(!HPK || (!WT && !WGRAD), "packed h: forward products only");
   static_assert(BW == 256 && (BT == 256 || (BT == 320 && !WGRAD)), "tiles are 256 x 256, or 256 x 320 but for WGRAD");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int AB = BW / 32;               // weight blocks per wavefront
@@ -100,6 +107,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   __shared__ __attribute__((aligned(16))) uint8_t smem[WGRAD ? SB : 4 * SB];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_tile0[kMaxExperts + 1];
+  __shared__ int32_t s_hpk0[HPK ? kMaxExperts + 1 : 1];  // HPK: first packed row of each group
   // WGRAD's other three stages are separate arrays, so that in its steady-state loop (below) the
   // compiler can tell, for a stage named statically, that the direct loads in flight into the other
   // stages do not write what it reads; the other modes keep the four stages in smem
@@ -121,6 +129,13 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       acc += WGRAD ? 0 : (s_off[e + 1] - s_off[e] + BT - 1) / BT * NT;
     }
     s_tile0[E] = acc;
+    if constexpr (HPK) {
+      int p0 = 0;
+      for (int e = 0; e < E; ++e) {
+        s_hpk0[e] = p0;
+        p0 += (s_off[e + 1] - s_off[e] + 15) & ~15;
+      }
+    }
   }
   __syncthreads();
   // Split-K (down projection only): every tile is computed as `ksplit` independent k-ranges;
@@ -181,6 +196,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   nrows = __builtin_amdgcn_readfirstlane(nrows);
   kcol0 = __builtin_amdgcn_readfirstlane((int)kcol0);
   nsteps_all = __builtin_amdgcn_readfirstlane(nsteps_all);
+  // HPK: packed 16-row block of the tile's first row (tiles start 16-aligned within their group)
+  const int pb0 = HPK ? (s_hpk0[e] + r0 - s_off[e]) >> 4 : 0;
   // token blocks of this wavefront that hold at least one row of the group
   const int nbv = min(BB, max(0, ((nrows + 15) / 16 - wt + 3) / 4));
   const int n0 = nt * NW;
@@ -286,7 +303,9 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       for (int i = 0; i < TI; ++i)
         if (i < ntl)  // the loaded fragments are the first ntl slots (blocks grow with i)
           __builtin_amdgcn_global_load_lds(
-              (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
+              (HPK && !SWIGLU)  // the down product reads packed h; the up products read x rows
+                  ? (const void*)(act + ((int64_t)(pb0 + wave + 8 * i) * (K / 32) + s) * 512 + lane * 8)
+                  : (const void*)(act + (int64_t)trow[i] * K + kcol0 + (int64_t)s * 32 + (lane >> 4) * 8),
               (lds_ptr)(base + WPB + (wave + 8 * i) * 1024), 16, 0, 0);
     }
   };
@@ -551,6 +570,10 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
 
   // Epilogue: lane l holds token (l%16) of each token block and weight rows 4*(l/16)..+3.
   const int li = lane & 15, lg = lane >> 4;
+  // HPK: element offset in packed h of the 4 columns f..f+3 (f % 4 == 0) of token block tb's row li
+  auto hpk_off = [&](int tb, int f) -> int64_t {
+    return (((int64_t)(pb0 + tb) * (N / 32) + (f >> 5)) * 64 + li + 16 * ((f & 31) >> 3)) * 8 + (f & 7);
+  };
   if constexpr (SWIGLU && sizeof(OutT) == 4) {
     // pre-activation pair (backward pass): a = x.w1^T to out, b = x.w3^T to part, both fp32
 #pragma unroll
@@ -569,7 +592,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) hv[q] = silu_t(acc[a][b][q]) * v[q];
-          *reinterpret_cast<u32x2_t*>(hout + o) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          const int64_t oh = HPK ? hpk_off(wt + 4 * b, n0 + (wr * (AB / 2) + a) * 16 + 4 * lg) : o;
+          *reinterpret_cast<u32x2_t*>(hout + oh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
         }
       }
   } else if constexpr (SWIGLU) {
@@ -583,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = silu_t(acc[a][b][q]) * acc[a + AB / 2][b][q];
-        *reinterpret_cast<u32x2_t*>(out + (int64_t)(r0 + tr) * N + f) =
+        *reinterpret_cast<u32x2_t*>(out + (HPK ? hpk_off(wt + 4 * b, f) : (int64_t)(r0 + tr) * N + f)) =
             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   } else {
@@ -600,14 +624,14 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   }
 }
 
-template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false>
+template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false, bool HPK = false>
 void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
                  const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s,
                  void* hout = nullptr) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT>), dim3((unsigned)grid), dim3(512), 0, s,
+  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT, HPK>), dim3((unsigned)grid), dim3(512), 0, s,
                 static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
                 static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0, N,
                 static_cast<bf16_t*>(hout));
@@ -657,18 +681,27 @@ void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int 
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
-                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t s) {
-  if (layout == kPacked)
+                    int F, int E, const void* w1, const void* w3, void* h, hipStream_t s, bool hpk) {
+  if (layout == kPacked && hpk)
+    launch_tile<256, kBT, true, true, bf16_t, false, true>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+  else if (layout == kPacked)
     launch_tile<256, kBT, true, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
+  else if (hpk)
+    launch_tile<256, kBT, false, true, bf16_t, false, true>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr,
+                                                            s);
   else
     launch_tile<256, kBT, false, true, bf16_t>(act, row_src, offsets, rows, E, w1, w3, h, d, F, 1, nullptr, s);
 }
 
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t s,
-                         void* h) {
-  if (layout == kPacked)
+                         void* h, bool hpk) {
+  if (layout == kPacked && hpk)
+    launch_tile<256, kBT, true, true, float, false, true>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+  else if (layout == kPacked)
     launch_tile<256, kBT, true, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+  else if (hpk)
+    launch_tile<256, kBT, false, true, float, false, true>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
   else
     launch_tile<256, kBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
 }
@@ -680,10 +713,16 @@ void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
-                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t s) {
-  if (layout == kPacked)
+                      const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t s, bool hpk) {
+  if (layout == kPacked && hpk)
+    launch_tile<256, kBT, true, false, float, false, true>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d,
+                                                           ksplit, y_part, s);
+  else if (layout == kPacked)
     launch_tile<256, kBT, true, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
                                                 y_part, s);
+  else if (hpk)
+    launch_tile<256, kBT, false, false, float, false, true>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d,
+                                                            ksplit, y_part, s);
   else
     launch_tile<256, kBT, false, false, float>(h, nullptr, offsets, rows, E, w2, nullptr, y_perm, F, d, ksplit,
                                                  y_part, s);

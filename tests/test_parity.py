@@ -481,6 +481,11 @@ FUSED = {
     "fused_decode": mi.Workload("fused_decode", T=32, d=4096, F=14336, dtype="bf16", seed=202),
     "fused_t1": mi.Workload("fused_t1", T=1, d=256, F=256, dtype="bf16", seed=635),
     "fused_t64_e16_k8": mi.Workload("fused_t64_e16_k8", T=64, d=192, F=192, E=16, K=8, dtype="bf16", seed=636),
+    # the tiled path (moe_forward keeps h fragment-packed between its two products, the stage call
+    # writes it row-major); shapes whose down projection takes one k-range, as the stage call does
+    "fused_tiled_e4": mi.Workload("fused_tiled_e4", T=700, d=256, F=512, E=4, K=2, dtype="bf16", seed=637),
+    "fused_tiled_skew": mi.Workload("fused_tiled_skew", T=2000, d=256, F=256, E=8, K=2, dtype="bf16", skew_bias=True,
+                                    seed=638),
 }
 
 
