@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "train", "block"], default="forward",
                    help="time moe_forward (default), moe_backward (gradients of the layer) or moe_block_forward "
                         "(decoder block: attention and the layer; workloads block_T*)")
+    p.add_argument("--weight-layout", choices=["packed", "rowmajor"], default="packed",
+                   help="backward and train passes: expert weights (and the weight gradients) fragment-packed "
+                        "(default) or row-major")
     return p.parse_args()
 
 
@@ -328,7 +331,9 @@ def backward_bench(args, w, train=False):
     """One step = one moe_backward call (routing and expert pre-activations recomputed from x; dx,
     dW_g, dw1, dw3, dw2 in fp32) over the workload's tokens, inputs resident in HBM.
     train: one step = moe_forward keeping the expert pre-activations (moe_opts.activations) and
-    moe_backward reading them, row-major weights (the single copy both calls take)."""
+    moe_backward reading them. The expert weights are one copy both calls take, fragment-packed at
+    load time (the weight gradients then come out in the same packed order, as an elementwise
+    optimizer step on the packed weights wants them) or row-major (--weight-layout rowmajor)."""
     import numpy as np
     import torch
 
@@ -342,9 +347,17 @@ def backward_bench(args, w, train=False):
             return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
         return torch.from_numpy(a).to("cuda")
 
-    dims = moe.Dims(w.T, w.d, w.F, w.E, w.K, moe.MOE_BF16, moe.MOE_LAYOUT_ROWMAJOR)
+    packed = args.weight_layout == "packed"
+    dims = moe.Dims(w.T, w.d, w.F, w.E, w.K, moe.MOE_BF16,
+                    moe.MOE_LAYOUT_PACKED if packed else moe.MOE_LAYOUT_ROWMAJOR)
     W = mi.layer_weights(w)
     L = {k: (dev(v) if v is not None else None) for k, v in W.items()}
+    if packed:
+        for name, which in (("w1", moe.MOE_W_UP), ("w3", moe.MOE_W_UP), ("w2", moe.MOE_W_DOWN)):
+            pk = torch.empty_like(L[name])  # load-time weight rearrangement, not timed
+            moe.moe_pack_weights(dims, which, L[name], pk)
+            L[name] = pk
+        torch.cuda.synchronize()
     x_host, dy_host = mi.tokens(w), mi.upstream_grad(w)
     x, dy = dev(x_host), dev(dy_host)
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -407,7 +420,9 @@ def backward_bench(args, w, train=False):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens and upstream gradient, N(0,1/fan_in) weights)",
         "config": {"workload": w.name, "pass": "train" if train else "backward", "T": w.T, "d": w.d, "F": w.F,
-                   "E": w.E, "K": w.K, "weight_layout": "row-major", "parallelism": "single GPU"},
+                   "E": w.E, "K": w.K,
+                   "weight_layout": "fragment-packed weights and weight gradients" if packed else "row-major",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": ("moe_forward + moe_backward, whole step" if train else "moe_backward, whole call")

@@ -221,12 +221,18 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const moe_opts* opts, const
  *   dw2[e] = sum (g_k dy) h_k^T,  dw1[e] = sum da_k x^T,  dw3[e] = sum db_k x^T,  dW_g = x^T dlogit
  * The routing is recomputed from x; a_k, b_k are too, unless opts->activations holds them from a
  * moe_forward call on the same inputs.
- *   x, w_gate, w1, w3, w2  as in moe_forward (dims->dtype = MOE_BF16, weights row-major)
+ *   x, w_gate, w1, w3, w2  as in moe_forward (dims->dtype = MOE_BF16; weights row-major, or
+ *                          fragment-packed with weight_layout = MOE_LAYOUT_PACKED)
  *   dy       [T][d]    fp32 in   gradient of the loss with respect to y
  *   dx       [T][d]    fp32 out
  *   dw_gate  [d][E]    fp32 out
  *   dw1, dw3 [E][F][d] fp32 out  (overwritten; an expert without tokens gets zeros)
  *   dw2      [E][d][F] fp32 out
+ *                          With MOE_LAYOUT_PACKED, dw1, dw3 and dw2 come out in the element order of
+ *                          the packed bf16 weights: gradient W[e][n][k] at the index that
+ *                          moe_pack_weights gives bf16 W[e][n][k] (V = 8), so gradient element i
+ *                          belongs to packed weight element i (an elementwise optimizer step can
+ *                          run on the packed weights directly).
  *   dlogits  [T][E]    fp32 out  optional (NULL = not written): gradient of the logits,
  *                                zero for the experts not kept
  *   workspace: >= moe_backward_workspace_bytes(dims) bytes of device memory, 256-byte aligned
@@ -234,8 +240,9 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const moe_opts* opts, const
  * even); all sums are fp32 in a fixed order, so results are reproducible bit for bit.
  * opts: gate_bias and activations as in the forward; y_dtype, accumulate and stage_events are
  * ignored.
- * Supported: dims->dtype = MOE_BF16, weight_layout = MOE_LAYOUT_ROWMAJOR, d and F multiples of 256
- * (with the general limits above); other valid arguments return MOE_ERR_UNSUPPORTED. */
+ * Supported: dims->dtype = MOE_BF16, either weight layout, d and F multiples of 256 (with the
+ * general limits above); other valid arguments return MOE_ERR_UNSUPPORTED. Packed and row-major
+ * weights give the same gradients bit for bit (up to the order of dw1, dw3, dw2). */
 size_t moe_backward_workspace_bytes(const moe_dims* dims);
 moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* x, const void* w_gate, const void* w1,
                         const void* w3, const void* w2, const float* dy, float* dx, float* dw_gate, float* dw1,

@@ -142,8 +142,6 @@ BwdWorkspace bwd_layout(const moe_dims& m) {
 
 moe_status check_backward_sizes(const moe_dims& m) {
   if (m.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass supports bf16 only (dtype = %d)", m.dtype);
-  if (m.weight_layout != MOE_LAYOUT_ROWMAJOR)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward pass takes row-major weights (weight_layout = %d)", m.weight_layout);
   if (m.d % 256 != 0 || m.F % 256 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs d and F multiples of 256 (d = %d, F = %d)", m.d, m.F);
   return MOE_OK;
@@ -539,35 +537,37 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   float* dxp = static_cast<float*>(at(L.dxp));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t S = m.T * m.K;
-  const int rm = MOE_LAYOUT_ROWMAJOR;
+  const int lay = m.weight_layout;
+  const bool pk = lay == MOE_LAYOUT_PACKED;  // packed weights: gradients in the same packed order
 
   // Every product below runs on the LDS-tiled kernels (any group size is handled; token blocks past
-  // a group's end cost no MFMAs); the ones on transposed weights read w2 and w1, w3 as they lie.
+  // a group's end cost no MFMAs); the ones on transposed weights read w2 and w1, w3 as they lie
+  // (row-major or fragment-packed).
   // forward pieces: routing, permutation, gathered rows, pre-activations a = x.w1^T, b = x.w3^T
   moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
                     nullptr, s);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
-  if (!saved) moe::launch_tile_up_pair(rm, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
+  if (!saved) moe::launch_tile_up_pair(lay, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
   MOE_TRY(check_launch("moe_backward (recompute)"));
   // dh' = w2^T dy per row (w2 [E][d][F] is the transposed weight of this product), then the SwiGLU
   // and softmax derivatives
   moe::launch_gather_dy(dy, row_token, token_row, topk_w, m.K, S, m.d, at(L.dy_perm), at(L.do_perm), s);
-  moe::launch_tile_wt(at(L.dy_perm), offsets, S, m.F, m.d, m.E, w2, nullptr, dhp, 1, nullptr, s);
+  moe::launch_tile_wt(lay, at(L.dy_perm), offsets, S, m.F, m.d, m.E, w2, nullptr, dhp, 1, nullptr, s);
   moe::launch_swiglu_bwd(A, B, dhp, row_token, token_row, topk_w, m.K, S, m.F, at(L.h), at(L.dab), dg, s);
   moe::launch_router_bwd(dg, token_row, topk_idx, topk_w, m.T, m.E, m.K, dlog, s);
   MOE_TRY(check_launch("moe_backward (dgrad)"));
   // dx = sum_k (w1^T da + w3^T db) + W_g dlogit; dW_g = x^T dlogit
   float* dxp_part = static_cast<float*>(at(L.dxp_part));
-  moe::launch_tile_wt(at(L.dab), offsets, S, m.d, 2 * m.F, m.E, w1, w3, dxp, L.dx_ksplit, dxp_part, s);
+  moe::launch_tile_wt(lay, at(L.dab), offsets, S, m.d, 2 * m.F, m.E, w1, w3, dxp, L.dx_ksplit, dxp_part, s);
   moe::launch_dx(dxp, dxp_part, L.dx_ksplit - 1, token_row, dlog, w_gate, m.T, m.d, m.E, m.K, dx, s);
   moe::launch_dwgate(x, dlog, m.T, m.d, m.E, static_cast<float*>(at(L.dwg_part)), dw_gate, s);
   MOE_TRY(check_launch("moe_backward (dx)"));
   // expert weight gradients: products over each group's rows, read as they lie
   const uint16_t* dab = static_cast<const uint16_t*>(at(L.dab));  // bf16 [T*K][2F]
-  moe::launch_tile_wgrad(dab, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw1, s);
-  moe::launch_tile_wgrad(dab + m.F, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw3, s);
-  moe::launch_tile_wgrad(at(L.do_perm), m.d, m.d, at(L.h), m.F, m.F, offsets, m.E, dw2, s);
+  moe::launch_tile_wgrad(dab, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw1, s, pk);
+  moe::launch_tile_wgrad(dab + m.F, m.F, 2 * m.F, at(L.x_perm), m.d, m.d, offsets, m.E, dw3, s, pk);
+  moe::launch_tile_wgrad(at(L.do_perm), m.d, m.d, at(L.h), m.F, m.F, offsets, m.E, dw2, s, pk);
   return check_launch("moe_backward (weight gradients)");
 }
 

@@ -72,11 +72,11 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F);
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
                     int F, int E, const void* w1, const void* w3, void* h, hipStream_t stream, bool hpk = false);
 // Grouped product with transposed weights (backward pass): out[r][n] = sum_k act[r][k] W_e[k][n] for the
-// rows r of group e, W_e [K][N] row-major; wa holds k < K/2 and wb the rest when wb is given (wb
-// NULL: wa holds all K). fp32 out, split into ksplit k-ranges as launch_tile_down. N multiple of 256,
-// K of 64 (of 128 with wb).
-void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
-                    const void* wb, float* out, int ksplit, float* part, hipStream_t stream);
+// rows r of group e, W_e [K][N] row-major (kRowMajor) or fragment-packed as [K][N] (kPacked); wa holds
+// k < K/2 and wb the rest when wb is given (wb NULL: wa holds all K). fp32 out, split into ksplit
+// k-ranges as launch_tile_down. N multiple of 256, K of 64 (of 128 with wb).
+void launch_tile_wt(int layout, const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E,
+                    const void* wa, const void* wb, float* out, int ksplit, float* part, hipStream_t stream);
 // The two pre-activations a = x.w1^T, b = x.w3^T (fp32) in one pass of the up tile, and, if h is
 // not null, h = bf16(silu(a) b) as the fused product forms it (the forward keeping activations).
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
@@ -87,9 +87,10 @@ void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t
 
 // Weight-gradient products of the backward pass (bf16 operands, fp32 out): for each expert e,
 // out[e][m][n] = sum over the rows r of e's group of p[r][m] * q[r][n], p and q group-sorted rows of
-// strides ldp and ldq. M and N multiples of 256.
+// strides ldp and ldq. M and N multiples of 256. packed_out: out[e] in the fragment-packed element
+// order of an [M][N] weight instead of row-major.
 void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int ldq, const int32_t* offsets, int E,
-                       float* out, hipStream_t stream);
+                       float* out, hipStream_t stream, bool packed_out = false);
 
 // Rearranges W[E][N][K] (row-major) into the fragment-packed layout.
 void launch_pack_weights(int dtype, const void* w, int E, int N, int K, void* w_packed, hipStream_t stream);

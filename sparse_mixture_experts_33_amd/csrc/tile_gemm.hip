@@ -72,7 +72,12 @@ __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 //
 // WT: the weight operand is stored transposed, [E][K][N] with the N columns contiguous (the layout
 // in which the backward pass holds w2 and w1, w3 for its products): wa holds k < KA = K/2 and wb
-// the rest when wb is given (KA = K otherwise).
+// the rest when wb is given (KA = K otherwise). With PACKED the [E][K][N] weights are
+// fragment-packed (1 KB fragments of 16 k rows x 32 n columns, as moe_pack_weights writes them
+// with N as the contiguous dimension): a k-step's 32 x 256 block is 16 whole fragments, which the
+// transposing reads take apart like the row-major block.
+// WGRAD with PACKED writes out[e] in that same fragment-packed element order ([M][N] weights:
+// 16 m rows x 32 n columns per 512-element fragment), so a gradient lines up with packed weights.
 // HPK: the hidden activations h between the two forward products are fragment-packed: the up
 // product stores h (and the pair product its h output) and the down product reads it as its token
 // operand in 1 KB fragments of 16 rows x 32 columns (lane l: row l % 16, columns 8 (l / 16)..+7),
@@ -88,8 +93,8 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
                                                            int64_t part_stride, int M, int ldw,
                                                            bf16_t* __restrict__ hout) {
-  static_assert(!WGRAD || (!SWIGLU && !PACKED && WT), "the weight-gradient mode reads both operands k-major");
-  static_assert(!WT || (!SWIGLU && !PACKED), "transposed weights: plain product only");
+  static_assert(!WGRAD || (!SWIGLU && WT), "the weight-gradient mode reads both operands k-major");
+  static_assert(!WT || !SWIGLU, "transposed weights: plain product only");
   static_assert(!HPK || (!WT && !WGRAD), "packed h: forward products only");
   static_assert(BW == 256 && (BT == 256 || (BT == 320 && !WGRAD)), "tiles are 256 x 256, or 256 x 320 but for WGRAD");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
@@ -276,8 +281,14 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       } else if constexpr (WT) {
         const bool second = wb && s * 32 >= KA;  // uniform over the step (KA is a multiple of 32)
         const bf16_t* w = second ? wb : wa;
-        const int64_t k = (int64_t)s * 32 - (second ? KA : 0) + kR[i];
-        src = w + ((int64_t)e * KA + k) * ldw + n0 + ck;
+        if constexpr (PACKED) {
+          // fragment (k block i, n block `wave`) of the step's 32 x 256 block
+          const int64_t kb = 2 * ((int64_t)s - (second ? KA / 32 : 0)) + i;
+          src = w + (((int64_t)e * (KA / 16) + kb) * (N / 32) + n0 / 32 + wave) * 512 + lane * 8;
+        } else {
+          const int64_t k = (int64_t)s * 32 - (second ? KA : 0) + kR[i];
+          src = w + ((int64_t)e * KA + k) * ldw + n0 + ck;
+        }
       } else {
         int blk = j;
         const bf16_t* w = wa;
@@ -289,7 +300,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         }
         src = w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kW32 + wl32;
       }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + j * (WT ? KSLOT : 1024)), 16, 0, 0);
+      // packed transposed weights: fragment j at j KB, the second k block 64 bytes further, so that the
+      // 16-lane groups of a transposing read that take rows 0-15 and 16-31 use different banks
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src, (lds_ptr)(base + (WT && PACKED && !WGRAD ? j * 1024 + i * 64 : j * (WT ? KSLOT : 1024))),
+          16, 0, 0);
     }
     if constexpr (WGRAD) {
 #pragma unroll
@@ -327,7 +342,15 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   };
   // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
   // fragment (block wt) in stage 0; the others are at the constant offsets in the reads below
-  const uint32_t aoff = WT ? lds0 + ktr + wr * 256 : lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
+  // packed transposed weights: lane (g, a, c) reads row 8g + a of the step (k block g/2, fragment row
+  // 8 (g%2) + a) and columns 4c..4c+3 of a 16-column block: fragment byte (c/2) 256 + row 16 + (c%2) 8;
+  // the wavefront's eight blocks (columns 128 wr + 16 a) are 512 bytes apart
+  constexpr bool kTrPk = WT && PACKED && !WGRAD;
+  constexpr int kTrA = kTrPk ? 512 : 32, kTrH = kTrPk ? 64 : 512;
+  const uint32_t ktrp = (uint32_t)((lane >> 5) * (8 * 1024 + 64) + ((lane >> 1) & 1) * 256 +
+                                   (8 * ((lane >> 4) & 1) + ((lane >> 2) & 3)) * 16 + (lane & 1) * 8);
+  const uint32_t aoff = WT ? lds0 + (kTrPk ? ktrp + wr * 4096 : ktr + wr * 256)
+                           : lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
   const uint32_t boff = WGRAD ? lds0 + WPB + ktr + wt * 32 : lds0 + WPB + wt * 1024 + lane * 16;
   // WGRAD steady state: four steps per iteration with the stages named statically and the
   // transposing fragment reads written as builtins, so that the compiler can schedule the reads of
@@ -391,26 +414,33 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
           // k-major weights: two transposing reads per fragment (rows 8g + a and 8g + a + 4)
           u32x2_t L0, L1, L2, L3, L4, L5, L6, L7, H0, H1, H2, H3, H4, H5, H6, H7;
 #define MOE_TR_A                                                                                              \
-  "ds_read_b64_tr_b16 %[l0], %[av] offset:0\n"                                                               \
-  "ds_read_b64_tr_b16 %[h0], %[av] offset:512\n"                                                             \
-  "ds_read_b64_tr_b16 %[l1], %[av] offset:32\n"                                                              \
-  "ds_read_b64_tr_b16 %[h1], %[av] offset:544\n"                                                             \
-  "ds_read_b64_tr_b16 %[l2], %[av] offset:64\n"                                                              \
-  "ds_read_b64_tr_b16 %[h2], %[av] offset:576\n"                                                             \
-  "ds_read_b64_tr_b16 %[l3], %[av] offset:96\n"                                                              \
-  "ds_read_b64_tr_b16 %[h3], %[av] offset:608\n"                                                             \
-  "ds_read_b64_tr_b16 %[l4], %[av] offset:128\n"                                                             \
-  "ds_read_b64_tr_b16 %[h4], %[av] offset:640\n"                                                             \
-  "ds_read_b64_tr_b16 %[l5], %[av] offset:160\n"                                                             \
-  "ds_read_b64_tr_b16 %[h5], %[av] offset:672\n"                                                             \
-  "ds_read_b64_tr_b16 %[l6], %[av] offset:192\n"                                                             \
-  "ds_read_b64_tr_b16 %[h6], %[av] offset:704\n"                                                             \
-  "ds_read_b64_tr_b16 %[l7], %[av] offset:224\n"                                                             \
-  "ds_read_b64_tr_b16 %[h7], %[av] offset:736\n"
+  "ds_read_b64_tr_b16 %[l0], %[av] offset:%[ol0]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h0], %[av] offset:%[oh0]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l1], %[av] offset:%[ol1]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h1], %[av] offset:%[oh1]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l2], %[av] offset:%[ol2]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h2], %[av] offset:%[oh2]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l3], %[av] offset:%[ol3]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h3], %[av] offset:%[oh3]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l4], %[av] offset:%[ol4]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h4], %[av] offset:%[oh4]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l5], %[av] offset:%[ol5]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h5], %[av] offset:%[oh5]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l6], %[av] offset:%[ol6]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h6], %[av] offset:%[oh6]\n"                                                           \
+  "ds_read_b64_tr_b16 %[l7], %[av] offset:%[ol7]\n"                                                           \
+  "ds_read_b64_tr_b16 %[h7], %[av] offset:%[oh7]\n"
 #define MOE_TR_OUT_A                                                                                          \
   [l0] "=&v"(L0), [l1] "=&v"(L1), [l2] "=&v"(L2), [l3] "=&v"(L3), [l4] "=&v"(L4), [l5] "=&v"(L5),            \
       [l6] "=&v"(L6), [l7] "=&v"(L7), [h0] "=&v"(H0), [h1] "=&v"(H1), [h2] "=&v"(H2), [h3] "=&v"(H3),         \
       [h4] "=&v"(H4), [h5] "=&v"(H5), [h6] "=&v"(H6), [h7] "=&v"(H7)
+// weight block a at a * kTrA bytes, its rows + 4 kTrH further (row-major slots / packed fragments)
+#define MOE_TR_IN_A                                                                                           \
+  [ol0] "i"(0 * kTrA), [ol1] "i"(1 * kTrA), [ol2] "i"(2 * kTrA), [ol3] "i"(3 * kTrA), [ol4] "i"(4 * kTrA),   \
+      [ol5] "i"(5 * kTrA), [ol6] "i"(6 * kTrA), [ol7] "i"(7 * kTrA), [oh0] "i"(0 * kTrA + kTrH),             \
+      [oh1] "i"(1 * kTrA + kTrH), [oh2] "i"(2 * kTrA + kTrH), [oh3] "i"(3 * kTrA + kTrH),                    \
+      [oh4] "i"(4 * kTrA + kTrH), [oh5] "i"(5 * kTrA + kTrH), [oh6] "i"(6 * kTrA + kTrH),                    \
+      [oh7] "i"(7 * kTrA + kTrH)
           if constexpr (WGRAD) {
             // k-major tokens too: blocks wt + 4b at 128-byte steps
             u32x2_t M0, M1, M2, M3, N0, N1, N2, N3;
@@ -426,7 +456,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                          "s_waitcnt lgkmcnt(0)\n"
                          : MOE_TR_OUT_A, [m0] "=&v"(M0), [m1] "=&v"(M1), [m2] "=&v"(M2), [m3] "=&v"(M3),
                            [n0] "=&v"(N0), [n1] "=&v"(N1), [n2] "=&v"(N2), [n3] "=&v"(N3)
-                         : [av] "v"(av), [bv] "v"(bv)
+                         : [av] "v"(av), [bv] "v"(bv), MOE_TR_IN_A
                          : "memory");
             B[0] = u32x4_t{M0[0], M0[1], N0[0], N0[1]};
             B[1] = u32x4_t{M1[0], M1[1], N1[0], N1[1]};
@@ -442,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                          "s_waitcnt lgkmcnt(0)\n"
                          : MOE_TR_OUT_A, [b0] "=&v"(B[0]), [b1] "=&v"(B[1]), [b2] "=&v"(B[2]), [b3] "=&v"(B[3]),
                            [b4] "=&v"(B[4])
-                         : [av] "v"(av), [bv] "v"(bv)
+                         : [av] "v"(av), [bv] "v"(bv), MOE_TR_IN_A
                          : "memory");
           } else {
             asm volatile(MOE_TR_A
@@ -452,11 +482,12 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                          "ds_read_b128 %[b3], %[bv] offset:12288\n"
                          "s_waitcnt lgkmcnt(0)\n"
                          : MOE_TR_OUT_A, [b0] "=&v"(B[0]), [b1] "=&v"(B[1]), [b2] "=&v"(B[2]), [b3] "=&v"(B[3])
-                         : [av] "v"(av), [bv] "v"(bv)
+                         : [av] "v"(av), [bv] "v"(bv), MOE_TR_IN_A
                          : "memory");
           }
 #undef MOE_TR_A
 #undef MOE_TR_OUT_A
+#undef MOE_TR_IN_A
           A[0] = u32x4_t{L0[0], L0[1], H0[0], H0[1]};
           A[1] = u32x4_t{L1[0], L1[1], H1[0], H1[1]};
           A[2] = u32x4_t{L2[0], L2[1], H2[0], H2[1]};
@@ -617,9 +648,13 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       for (int b = 0; b < BB; ++b) {
         const int tr = (wt + 4 * b) * 16 + li;
         if (tr >= nrows) continue;
-        const int n = n0 + (wr * AB + a) * 16 + 4 * lg;
-        store16(out + (int64_t)(r0 + tr) * N + n, u32x4_t{__float_as_uint(acc[a][b][0]), __float_as_uint(acc[a][b][1]),
-                                                          __float_as_uint(acc[a][b][2]), __float_as_uint(acc[a][b][3])});
+        const int n = n0 + (wr * AB + a) * 16 + 4 * lg, m = r0 + tr;
+        // WGRAD, PACKED: fragment-packed order (16 m rows x 32 n columns per fragment)
+        const int64_t o = (WGRAD && PACKED) ? ((int64_t)(m >> 4) * (N >> 5) + (n >> 5)) * 512 + ((n & 31) >> 3) * 128 +
+                                                  (m & 15) * 8 + (n & 7)
+                                            : (int64_t)m * N + n;
+        store16(out + o, u32x4_t{__float_as_uint(acc[a][b][0]), __float_as_uint(acc[a][b][1]),
+                                 __float_as_uint(acc[a][b][2]), __float_as_uint(acc[a][b][3])});
       }
   }
 }
@@ -671,13 +706,19 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
 }
 
 void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int ldq, const int32_t* offsets, int E,
-                       float* out, hipStream_t s) {
+                       float* out, hipStream_t s, bool packed_out) {
   const int64_t tiles = (int64_t)E * (M / 256) * (N / 256);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<256, 256, false, false, true, true, float>), dim3((unsigned)grid), dim3(512), 0, s,
-                static_cast<const bf16_t*>(p), static_cast<const int32_t*>(nullptr), offsets,
-                static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(nullptr), out, ldp, N, E, 1,
-                static_cast<float*>(nullptr), (int64_t)0, M, ldq, static_cast<bf16_t*>(nullptr));
+  auto go = [&](auto kernel) {
+    launch_kernel(kernel, dim3((unsigned)grid), dim3(512), 0, s, static_cast<const bf16_t*>(p),
+                  static_cast<const int32_t*>(nullptr), offsets, static_cast<const bf16_t*>(q),
+                  static_cast<const bf16_t*>(nullptr), out, ldp, N, E, 1, static_cast<float*>(nullptr), (int64_t)0, M,
+                  ldq, static_cast<bf16_t*>(nullptr));
+  };
+  if (packed_out)
+    go(tile_gemm_kernel<256, 256, true, false, true, true, float>);
+  else
+    go(tile_gemm_kernel<256, 256, false, false, true, true, float>);
 }
 
 void launch_tile_up(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int d,
@@ -706,10 +747,13 @@ void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, co
     launch_tile<256, kBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
 }
 
-void launch_tile_wt(const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E, const void* wa,
-                    const void* wb, float* out, int ksplit, float* part, hipStream_t s) {
-  launch_tile<256, kBT, false, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part,
-                                                      s);
+void launch_tile_wt(int layout, const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E,
+                    const void* wa, const void* wb, float* out, int ksplit, float* part, hipStream_t s) {
+  if (layout == kPacked)
+    launch_tile<256, kBT, true, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part, s);
+  else
+    launch_tile<256, kBT, false, false, float, true>(act, nullptr, offsets, rows, E, wa, wb, out, K, N, ksplit, part,
+                                                        s);
 }
 
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,

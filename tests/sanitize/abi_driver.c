@@ -70,8 +70,13 @@ int main(void) {
   /* backward */
   d = ok; d.dtype = MOE_F32;
   EXPECT(moe_backward(&d, NULL, p, p, p, p, p, p, p, p, p, p, p, NULL, p, 1 << 30, NULL), MOE_ERR_UNSUPPORTED);
-  d = ok; d.weight_layout = MOE_LAYOUT_PACKED;
-  EXPECT(moe_backward(&d, NULL, p, p, p, p, p, p, p, p, p, p, p, NULL, p, 1 << 30, NULL), MOE_ERR_UNSUPPORTED);
+  d = ok; d.weight_layout = 2; /* not a layout */
+  EXPECT(moe_backward(&d, NULL, p, p, p, p, p, p, p, p, p, p, p, NULL, p, 1 << 30, NULL), MOE_ERR_INVALID_ARG);
+  d = ok; d.weight_layout = MOE_LAYOUT_PACKED; /* either layout: the same workspace */
+  if (moe_backward_workspace_bytes(&d) != moe_backward_workspace_bytes(&ok)) {
+    fprintf(stderr, "FAILED moe_backward_workspace_bytes (packed)\n");
+    ++fails;
+  }
   if (moe_backward_workspace_bytes(&ok) == 0) { fprintf(stderr, "FAILED moe_backward_workspace_bytes\n"); ++fails; }
   EXPECT(moe_backward(&ok, NULL, p, p, p, p, p, p, p, p, p, p, p, NULL, p, 16, NULL), MOE_ERR_WORKSPACE);
   /* norm, attention, block */

@@ -158,9 +158,13 @@ def test_backward_validation():
     L = moe.lib()
     ok = moe_dims(64, 256, 512, 8, 2, 1, 0)
     assert L.moe_backward_workspace_bytes(ctypes.byref(ok)) > 0
-    # supported sizes only: bf16, row-major weights, d and F multiples of 256
-    for bad in (moe_dims(64, 256, 512, 8, 2, 0, 0), moe_dims(64, 256, 512, 8, 2, 1, 1),
-                moe_dims(64, 192, 512, 8, 2, 1, 0), moe_dims(64, 256, 448, 8, 2, 1, 0)):
+    # either weight layout (the packed one gives the same workspace)
+    pk = moe_dims(64, 256, 512, 8, 2, 1, 1)
+    assert L.moe_backward_workspace_bytes(ctypes.byref(pk)) == L.moe_backward_workspace_bytes(ctypes.byref(ok))
+    assert _backward(moe_dims(64, 256, 512, 8, 2, 1, 2)) == 1        # not a layout
+    # supported sizes only: bf16, d and F multiples of 256
+    for bad in (moe_dims(64, 256, 512, 8, 2, 0, 0), moe_dims(64, 192, 512, 8, 2, 1, 0),
+                moe_dims(64, 256, 448, 8, 2, 1, 0)):
         assert L.moe_backward_workspace_bytes(ctypes.byref(bad)) == 0
         assert _backward(bad) == 2
     assert _backward(moe_dims(64, 256, 512, 8, 9, 1, 0)) == 1       # K > E

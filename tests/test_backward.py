@@ -58,15 +58,28 @@ def dy_for(w):
     return mi.upstream_grad(w)
 
 
-def gpu_backward(M, w, W, x, dy, bias, dlogits=True):
-    dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16)
+def packed_order(a):
+    """[E][N][K] -> flat, in the element order moe.h gives the packed bf16 weights (V = 8): element
+    (e, n, k) at ((e (N/16) + n/16) (K/32) + k/32) 512 + (n%16 + 16 ((k/8)%4)) 8 + k%8."""
+    E, N, K = a.shape
+    return a.reshape(E, N // 16, 16, K // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+
+
+def gpu_backward(M, w, W, x, dy, bias, dlogits=True, packed=False):
+    dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16, M.MOE_LAYOUT_PACKED if packed else M.MOE_LAYOUT_ROWMAJOR)
+    wd = {k: dev(W[k]) for k in ("w1", "w3", "w2")}
+    if packed:
+        for k, which in (("w1", M.MOE_W_UP), ("w3", M.MOE_W_UP), ("w2", M.MOE_W_DOWN)):
+            out = torch.empty_like(wd[k])
+            M.moe_pack_weights(dm, which, wd[k], out)
+            wd[k] = out
     ws = torch.empty(M.moe_backward_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
     out = {"dx": torch.empty((w.T, w.d), **f32), "dw_gate": torch.empty((w.d, w.E), **f32),
            "dw1": torch.empty((w.E, w.F, w.d), **f32), "dw3": torch.empty((w.E, w.F, w.d), **f32),
            "dw2": torch.empty((w.E, w.d, w.F), **f32),
            "dlogits": torch.empty((w.T, w.E), **f32) if dlogits else None}
-    M.moe_backward(dm, dev(x), dev(W["w_gate"]), dev(W["w1"]), dev(W["w3"]), dev(W["w2"]), dev(dy), out["dx"],
+    M.moe_backward(dm, dev(x), dev(W["w_gate"]), wd["w1"], wd["w3"], wd["w2"], dev(dy), out["dx"],
                    out["dw_gate"], out["dw1"], out["dw3"], out["dw2"], ws, dlogits=out["dlogits"],
                    gate_bias=None if bias is None else dev(bias))
     torch.cuda.synchronize()
@@ -99,6 +112,27 @@ def test_backward_small(M, name):
         assert not np.any(idx == 5)
         for k in ("dw1", "dw3", "dw2"):
             assert np.all(got[k][5] == 0.0), k
+
+
+@pytest.mark.parametrize("name", ["tiled_e4", "e16_k4_bias", "empty_expert"])
+def test_backward_packed_weights(M, name):
+    """Fragment-packed weights give the row-major pass's gradients bit for bit: dx, dlogits and dW_g
+    as they are, dw1, dw3, dw2 in the packed element order of the weights (the products run the same
+    sums in the same order; only the weight loads and the gradient stores are addressed differently)."""
+    c = CASES[name]
+    w = c["w"]
+    say(f"[backward] packed weights, {name} T={w.T} d={w.d} F={w.F} E={w.E} K={w.K}")
+    W = mi.layer_weights(w)
+    x = mi.tokens(w)
+    bias = make_bias(c["bias"], w.E, w.seed)
+    dy = dy_for(w)
+    rm = gpu_backward(M, w, W, x, dy, bias)
+    pk = gpu_backward(M, w, W, x, dy, bias, packed=True)
+    for k in ("dx", "dlogits", "dw_gate"):
+        assert np.array_equal(rm[k], pk[k]), k
+    for k in ("dw1", "dw3", "dw2"):
+        assert pk[k].shape == rm[k].shape
+        assert np.array_equal(packed_order(rm[k]), pk[k].reshape(-1)), k
 
 
 def test_backward_is_deterministic(M):

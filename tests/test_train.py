@@ -61,15 +61,14 @@ def run(M, w, W, x, packed, keep, bias=None):
     ws = torch.empty(M.moe_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
     b = None if bias is None else dev(bias)
     M.moe_forward(dm, xd, fw["w_gate"], fw["w1"], fw["w3"], fw["w2"], y, ws, gate_bias=b, activations=act)
-    # the backward pass takes row-major weights
-    db = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16)
-    bws = torch.empty(M.moe_backward_workspace_bytes(db), dtype=torch.uint8, device="cuda")
+    # the backward pass takes the same weights (packed ones give the gradients in packed order)
+    bws = torch.empty(M.moe_backward_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
     g = {"dx": torch.empty((w.T, w.d), **f32), "dw_gate": torch.empty((w.d, w.E), **f32),
          "dw1": torch.empty((w.E, w.F, w.d), **f32), "dw3": torch.empty((w.E, w.F, w.d), **f32),
          "dw2": torch.empty((w.E, w.d, w.F), **f32), "dlogits": torch.empty((w.T, w.E), **f32)}
     dy = dev(mi.upstream_grad(w))
-    M.moe_backward(db, xd, dW["w_gate"], dW["w1"], dW["w3"], dW["w2"], dy, g["dx"], g["dw_gate"], g["dw1"],
+    M.moe_backward(dm, xd, fw["w_gate"], fw["w1"], fw["w3"], fw["w2"], dy, g["dx"], g["dw_gate"], g["dw1"],
                    g["dw3"], g["dw2"], bws, dlogits=g["dlogits"], gate_bias=b, activations=act)
     torch.cuda.synchronize()
     out = {k: host(v) for k, v in g.items()}
