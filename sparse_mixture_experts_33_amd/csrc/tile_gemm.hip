@@ -300,11 +300,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         }
         src = w + wrow0 + (int64_t)blk * 16 * K + (int64_t)s * kW32 + wl32;
       }
-      // packed transposed weights: fragment j at j KB, the second k block 64 bytes further, so that the
-      // 16-lane groups of a transposing read that take rows 0-15 and 16-31 use different banks
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src, (lds_ptr)(base + (WT && PACKED && !WGRAD ? j * 1024 + i * 64 : j * (WT ? KSLOT : 1024))),
-          16, 0, 0);
+      // packed transposed weights: the fragments in pairs (n blocks 2p', 2p' + 1 of a k block) of 2112
+      // bytes, the odd one 1088 bytes into its pair (see the reads)
+      const int dst = WT && PACKED && !WGRAD ? (i * 4 + (wave >> 1)) * 2112 + (wave & 1) * 1088
+                                             : j * (WT ? KSLOT : 1024);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + dst), 16, 0, 0);
     }
     if constexpr (WGRAD) {
 #pragma unroll
@@ -342,14 +342,20 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   };
   // LDS byte addresses of this lane's first weight fragment (block wblock(0)) and first token
   // fragment (block wt) in stage 0; the others are at the constant offsets in the reads below
-  // packed transposed weights: lane (g, a, c) reads row 8g + a of the step (k block g/2, fragment row
-  // 8 (g%2) + a) and columns 4c..4c+3 of a 16-column block: fragment byte (c/2) 256 + row 16 + (c%2) 8;
-  // the wavefront's eight blocks (columns 128 wr + 16 a) are 512 bytes apart
+  // packed transposed weights: a 16-column block of the matrix cores takes 8 columns (chunk a % 4) of
+  // each of the n fragments 2 (a / 4) and 2 (a / 4) + 1 of the wavefront (columns 128 wr + 64 (a / 4) +
+  // 32 h + 8 (a % 4) + 0..7, h = 0, 1). A pair of fragments takes 2112 bytes of the stage, its odd one
+  // 1088 bytes in (64 bytes further modulo 256). Lane (g, a', c) of a transposing read reads row 8g + a'
+  // of the step (k block g / 2, fragment row 8 (g % 2) + a') and 4 columns of fragment h = c / 2 at chunk
+  // byte 16 row + 8 (c % 2): the 32 lanes of each half-wavefront touch 256 different bytes (with both
+  // halves of a block in one fragment, lanes 256 bytes apart would share banks)
   constexpr bool kTrPk = WT && PACKED && !WGRAD;
-  constexpr int kTrA = kTrPk ? 512 : 32, kTrH = kTrPk ? 64 : 512;
-  const uint32_t ktrp = (uint32_t)((lane >> 5) * (8 * 1024 + 64) + ((lane >> 1) & 1) * 256 +
+  static_assert(!kTrPk || AB == 8, "packed transposed weights: 256-column weight tiles");
+  constexpr int kTrH = kTrPk ? 64 : 512;  // rows + 4 of a read
+  auto tr_off = [](int a) constexpr { return kTrPk ? (a / 4) * 2112 + (a % 4) * 256 : a * 32; };  // block a
+  const uint32_t ktrp = (uint32_t)((lane >> 5) * (4 * 2112) + ((lane >> 1) & 1) * 1088 +
                                    (8 * ((lane >> 4) & 1) + ((lane >> 2) & 3)) * 16 + (lane & 1) * 8);
-  const uint32_t aoff = WT ? lds0 + (kTrPk ? ktrp + wr * 4096 : ktr + wr * 256)
+  const uint32_t aoff = WT ? lds0 + (kTrPk ? ktrp + wr * (2 * 2112) : ktr + wr * 256)
                            : lds0 + lane * 16 + (SWIGLU ? wr * 4 : wr * 8) * 1024;
   const uint32_t boff = WGRAD ? lds0 + WPB + ktr + wt * 32 : lds0 + WPB + wt * 1024 + lane * 16;
   // WGRAD steady state: four steps per iteration with the stages named statically and the
@@ -434,13 +440,13 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   [l0] "=&v"(L0), [l1] "=&v"(L1), [l2] "=&v"(L2), [l3] "=&v"(L3), [l4] "=&v"(L4), [l5] "=&v"(L5),            \
       [l6] "=&v"(L6), [l7] "=&v"(L7), [h0] "=&v"(H0), [h1] "=&v"(H1), [h2] "=&v"(H2), [h3] "=&v"(H3),         \
       [h4] "=&v"(H4), [h5] "=&v"(H5), [h6] "=&v"(H6), [h7] "=&v"(H7)
-// weight block a at a * kTrA bytes, its rows + 4 kTrH further (row-major slots / packed fragments)
+// weight block a at tr_off(a) bytes, its rows + 4 kTrH further (row-major slots / packed fragments)
 #define MOE_TR_IN_A                                                                                           \
-  [ol0] "i"(0 * kTrA), [ol1] "i"(1 * kTrA), [ol2] "i"(2 * kTrA), [ol3] "i"(3 * kTrA), [ol4] "i"(4 * kTrA),   \
-      [ol5] "i"(5 * kTrA), [ol6] "i"(6 * kTrA), [ol7] "i"(7 * kTrA), [oh0] "i"(0 * kTrA + kTrH),             \
-      [oh1] "i"(1 * kTrA + kTrH), [oh2] "i"(2 * kTrA + kTrH), [oh3] "i"(3 * kTrA + kTrH),                    \
-      [oh4] "i"(4 * kTrA + kTrH), [oh5] "i"(5 * kTrA + kTrH), [oh6] "i"(6 * kTrA + kTrH),                    \
-      [oh7] "i"(7 * kTrA + kTrH)
+  [ol0] "i"(tr_off(0)), [ol1] "i"(tr_off(1)), [ol2] "i"(tr_off(2)), [ol3] "i"(tr_off(3)),                    \
+      [ol4] "i"(tr_off(4)), [ol5] "i"(tr_off(5)), [ol6] "i"(tr_off(6)), [ol7] "i"(tr_off(7)),               \
+      [oh0] "i"(tr_off(0) + kTrH), [oh1] "i"(tr_off(1) + kTrH), [oh2] "i"(tr_off(2) + kTrH),                 \
+      [oh3] "i"(tr_off(3) + kTrH), [oh4] "i"(tr_off(4) + kTrH), [oh5] "i"(tr_off(5) + kTrH),                 \
+      [oh6] "i"(tr_off(6) + kTrH), [oh7] "i"(tr_off(7) + kTrH)
           if constexpr (WGRAD) {
             // k-major tokens too: blocks wt + 4b at 128-byte steps
             u32x2_t M0, M1, M2, M3, N0, N1, N2, N3;
@@ -648,7 +654,10 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
       for (int b = 0; b < BB; ++b) {
         const int tr = (wt + 4 * b) * 16 + li;
         if (tr >= nrows) continue;
-        const int n = n0 + (wr * AB + a) * 16 + 4 * lg, m = r0 + tr;
+        // packed transposed weights: block a holds columns 64 (a/4) + 32 h + 8 (a%4) + 0..7 of the wavefront's
+        const int n = kTrPk ? n0 + wr * 128 + 64 * (a / 4) + 32 * (lg / 2) + 8 * (a % 4) + 4 * (lg % 2)
+                            : n0 + (wr * AB + a) * 16 + 4 * lg;
+        const int m = r0 + tr;
         // WGRAD, PACKED: fragment-packed order (16 m rows x 32 n columns per fragment)
         const int64_t o = (WGRAD && PACKED) ? ((int64_t)(m >> 4) * (N >> 5) + (n >> 5)) * 512 + ((n & 31) >> 3) * 128 +
                                                   (m & 15) * 8 + (n & 7)
