@@ -191,3 +191,42 @@ def test_backward_full_size_sampled(M):
     err = rel_err(got["dw_gate"], dwg_ref)
     say(f"  dw_gate vs x^T dlogits: {err:.3e}")
     assert err <= 1e-4
+
+
+def test_backward_packed_weights_full_size(M):
+    """The packed-weight pass at the Mixtral prefill shape (T=4096, d=4096, F=14336, E=8, K=2) against
+    the row-major pass on the same inputs, every element: dx, dlogits, dW_g equal, and dw1, dw3, dw2
+    equal after the row-major gradients are put in the packed order (compared on the GPU). The
+    row-major pass is pinned to the oracle by the sampled full-size test above."""
+    w = mi.WORKLOADS["prefill_T4096"]
+    say(f"[backward] packed weights, full size {w.name}")
+    W = mi.layer_weights(w)
+    x, dy = dev(mi.tokens(w)), dev(mi.upstream_grad(w))
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def run(packed):
+        dm = M.Dims(w.T, w.d, w.F, w.E, w.K, M.MOE_BF16, M.MOE_LAYOUT_PACKED if packed else M.MOE_LAYOUT_ROWMAJOR)
+        wd = {k: dev(W[k]) for k in ("w1", "w3", "w2")}
+        if packed:
+            for k, which in (("w1", M.MOE_W_UP), ("w3", M.MOE_W_UP), ("w2", M.MOE_W_DOWN)):
+                out = torch.empty_like(wd[k])
+                M.moe_pack_weights(dm, which, wd[k], out)
+                wd[k] = out
+        ws = torch.empty(M.moe_backward_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
+        g = {"dx": torch.empty((w.T, w.d), **f32), "dw_gate": torch.empty((w.d, w.E), **f32),
+             "dw1": torch.empty((w.E, w.F, w.d), **f32), "dw3": torch.empty((w.E, w.F, w.d), **f32),
+             "dw2": torch.empty((w.E, w.d, w.F), **f32), "dlogits": torch.empty((w.T, w.E), **f32)}
+        M.moe_backward(dm, x, dev(W["w_gate"]), wd["w1"], wd["w3"], wd["w2"], dy, g["dx"], g["dw_gate"], g["dw1"],
+                       g["dw3"], g["dw2"], ws, dlogits=g["dlogits"])
+        torch.cuda.synchronize()
+        return g
+
+    rm = run(False)
+    pk = run(True)
+    for k in ("dx", "dlogits", "dw_gate"):
+        assert torch.equal(rm[k], pk[k]), k
+    for k in ("dw1", "dw3", "dw2"):
+        E, N, K = rm[k].shape
+        order = rm[k].reshape(E, N // 16, 16, K // 32, 4, 8).permute(0, 1, 3, 4, 2, 5).reshape(-1)
+        assert torch.equal(order, pk[k].reshape(-1)), k
+        say(f"  {k}: all {E * N * K} entries equal in the packed order")
