@@ -200,10 +200,12 @@ moe_status moe_forward(const moe_dims* dims, const moe_opts* opts, const void* x
  * device and allocates nothing (no hipMalloc, hipFree or allocating library routine).
  *   Arguments as in moe_forward, minus workspace and workspace_bytes.
  *   Sizes whose moe_workspace_bytes() exceeds the scratch return MOE_ERR_WORKSPACE before anything
- *   is launched (at d = 4096, F = 14336, E = 8, K = 2 the limit is about 700 tokens: the decode
- *   batches; larger batches call moe_forward with a workspace).
+ *   is launched (at d = 4096, F = 14336, E = 8, K = 2 the limit is 517 tokens, the decode batches:
+ *   from 512 tokens the k-split partial sums of the tiled path join the workspace; larger batches
+ *   call moe_forward with a workspace).
  *   Every call on a device shares that device's scratch and leaves its contents behind; nothing in
- *   it needs to start at zero (every piece is written before it is read). Calls that overlap in time
+ *   it needs to start at zero (every value that enters a result is written before it is read; the
+ *   padding rows of the packed hidden activations are read but feed only discarded output rows). Calls that overlap in time
  *   on one device (on different streams, or from different host threads without ordering between
  *   their streams) race on the scratch and give undefined results; calls ordered on one stream are
  *   safe. Results are bit-identical to moe_forward's. */
