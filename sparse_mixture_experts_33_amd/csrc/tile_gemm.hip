@@ -21,7 +21,9 @@
 // address the 16 columns of row a, and lane i receives column i of the 4 rows, which is 4
 // consecutive k of output row i). Such a block is 16 slots of two 512-byte rows (rows r and r + 4,
 // r = (j & 3) + 8 (j >> 2) for slot j), 1056 bytes apart: the 16 rows one transposing read touches
-// then lie in 16 different slots, whose 32-byte offsets spread them over all banks.
+// then lie in 16 different slots, whose 32-byte offsets spread them over all banks. Packed
+// transposed weights arrive as 1 KB fragments of 16 k rows x 32 columns and are read the same way
+// (the fragment layout in the kernel below).
 //
 // Tiles are numbered expert-major, then in bands of 4 token tiles, then weight tile, then token
 // tile within the band, so that the 32 tiles an XCD runs at once share 4 token and 8 weight row
@@ -83,7 +85,8 @@ __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 // operand in 1 KB fragments of 16 rows x 32 columns (lane l: row l % 16, columns 8 (l / 16)..+7),
 // fragments of a 16-row block consecutive along F. Each group's rows start a new block: row r of
 // group e is packed row hpk_row0(e) + r - offsets[e], hpk_row0(e) = sum over e' < e of the group
-// sizes rounded up to 16 (packed rows past a group's end are never written nor stored from).
+// sizes rounded up to 16. Packed rows past a group's end are never written; the down product reads
+// them with their block, and the output rows they produce are not stored.
 template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT, bool HPK = false>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
