@@ -14,8 +14,9 @@
 //    per row, 16 bytes each); the k values a lane feeds to successive MFMAs are therefore a
 //    fixed permutation of the true k order, the same for A and B, so the contraction is
 //    unchanged; weights use non-temporal loads (read once);
-//  - the 4 wavefronts of a workgroup split K and their partial sums are added in LDS in a
-//    fixed order (wave 0 + 1 + 2 + 3), so results are reproducible bit for bit;
+//  - the 4 wavefronts of a workgroup split K, taking every fourth k-step each (so together they
+//    stream one contiguous run of each weight row block), and their partial sums are added in
+//    LDS in a fixed order (wave 0 + 1 + 2 + 3), so results are reproducible bit for bit;
 //  - the grid is persistent (as many workgroups as fit on the device at once); each workgroup
 //    walks items (row tile, 16 rows of W) with a stride of the grid size, mapping tiles to
 //    experts from `offsets` on the device (no host readback), so no workgroup waits in a
@@ -78,7 +79,10 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const T* __restrict__ 
   const int ntiles = s_tile0[E];
   const int NG = N / (16 * RB);
   const int nsteps = K / CK;
-  const int c_lo = wave * nsteps / NWAVES, c_hi = (wave + 1) * nsteps / NWAVES;
+  // wavefront w takes the k-steps w, w + 4, w + 8, ... (its i-th is step w + 4 i): the four
+  // wavefronts' loads of one round are then four consecutive steps, one contiguous run per weight
+  // row block, which streams from HBM faster than four runs a quarter of K apart
+  const int c_lo = 0, c_hi = (nsteps - wave + NWAVES - 1) / NWAVES;
 
   // Persistent loop over items (tile, 16*RB rows of W); consecutive workgroups take
   // consecutive row groups of the same tile, so the tile's token rows stay hot in L2.
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const T* __restrict__ 
       }
 
     using FragT = Frag<T, LPC, NTB, RB>;
-    auto load = [&](FragT& f, int c) {
+    auto load = [&](FragT& f, int i) {
+      const int c = wave + NWAVES * i;  // the k-step
       const int64_t ko = (int64_t)c * CK;
       // weights are read exactly once: non-temporal loads keep them from evicting the token rows
 #pragma unroll
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const T* __restrict__ 
       }
     }
 
-    // the 4 K-quarters are added in a fixed order: wave 0 + 1 + 2 + 3
+    // the 4 partial sums are added in a fixed order: wave 0 + 1 + 2 + 3
     if (wave > 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
