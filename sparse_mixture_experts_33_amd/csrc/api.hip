@@ -103,8 +103,8 @@ Workspace layout(const moe_dims& m) {
 
 // Backward workspace.
 struct BwdWorkspace {
-  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, A, B, dy_perm, do_perm, dhp, h,
-      dab, dg, dlog, dxp, dxp_part, dwg_part, total;
+  size_t topk_idx, topk_w, counts, offsets, row_token, token_row, x_perm, dy_perm, do_perm, dhp, h, dab, dgp,
+      row_g, sink, dg, dlog, dxp, dxp_part, dwg_part, total;
   int dx_ksplit;  // k-ranges of the product [da|db] . [w1|w3] (partials 1.. at dxp_part)
 };
 
@@ -123,13 +123,14 @@ BwdWorkspace bwd_layout(const moe_dims& m) {
   take(w.row_token, S * 4);
   take(w.token_row, S * 4);
   take(w.x_perm, S * d * 2);
-  take(w.A, S * F * 4);
-  take(w.B, S * F * 4);
   take(w.dy_perm, S * d * 2);
   take(w.do_perm, S * d * 2);
   take(w.dhp, S * F * 4);
   take(w.h, S * F * 2);
   take(w.dab, S * 2 * F * 2);
+  take(w.dgp, F / 64 * S * 4);
+  take(w.row_g, S * 4);
+  take(w.sink, 16);
   take(w.dg, S * 4);
   take(w.dlog, (size_t)m.T * E * 4);
   take(w.dxp, S * d * 4);
@@ -529,8 +530,7 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   int32_t* row_token = static_cast<int32_t*>(at(L.row_token));
   int32_t* token_row = static_cast<int32_t*>(at(L.token_row));
   const float* saved = opts ? opts->activations : nullptr;
-  float* A = saved ? const_cast<float*>(saved) : static_cast<float*>(at(L.A));
-  float* B = saved ? const_cast<float*>(saved) + (size_t)m.T * m.K * m.F : static_cast<float*>(at(L.B));
+  float* dgp = static_cast<float*>(at(L.dgp));
   float* dhp = static_cast<float*>(at(L.dhp));
   float* dg = static_cast<float*>(at(L.dg));
   float* dlog = dlogits ? dlogits : static_cast<float*>(at(L.dlog));
@@ -543,18 +543,24 @@ moe_status moe_backward(const moe_dims* dims, const moe_opts* opts, const void* 
   // Every product below runs on the LDS-tiled kernels (any group size is handled; token blocks past
   // a group's end cost no MFMAs); the ones on transposed weights read w2 and w1, w3 as they lie
   // (row-major or fragment-packed).
-  // forward pieces: routing, permutation, gathered rows, pre-activations a = x.w1^T, b = x.w3^T
+  // forward pieces: routing, permutation, gathered rows
   moe::launch_route(m.dtype, x, w_gate, opts ? opts->gate_bias : nullptr, m.T, m.d, m.E, m.K, topk_idx, topk_w,
                     nullptr, s);
   moe::launch_permute_index(topk_idx, m.T, m.E, m.K, counts, offsets, row_token, token_row, s);
   moe::launch_gather_rows(x, row_token, S, (int64_t)m.d * 2, at(L.x_perm), s);
-  if (!saved) moe::launch_tile_up_pair(lay, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, A, B, s);
-  MOE_TRY(check_launch("moe_backward (recompute)"));
-  // dh' = w2^T dy per row (w2 [E][d][F] is the transposed weight of this product), then the SwiGLU
-  // and softmax derivatives
-  moe::launch_gather_dy(dy, row_token, token_row, topk_w, m.K, S, m.d, at(L.dy_perm), at(L.do_perm), s);
+  // dh' = w2^T dy per row (w2 [E][d][F] is the transposed weight of this product)
+  float* row_g = static_cast<float*>(at(L.row_g));
+  moe::launch_gather_dy(dy, row_token, token_row, topk_w, m.K, S, m.d, at(L.dy_perm), at(L.do_perm), row_g, s);
   moe::launch_tile_wt(lay, at(L.dy_perm), offsets, S, m.F, m.d, m.E, w2, nullptr, dhp, 1, nullptr, s);
-  moe::launch_swiglu_bwd(A, B, dhp, row_token, token_row, topk_w, m.K, S, m.F, at(L.h), at(L.dab), dg, s);
+  // the SwiGLU derivative: from the kept pre-activations, or in the epilogue of their recomputation
+  // (a = x.w1^T, b = x.w3^T never leave the registers); then the softmax derivative
+  if (saved)
+    moe::launch_swiglu_bwd(saved, saved + (size_t)S * m.F, dhp, row_token, token_row, topk_w, m.K, S, m.F, at(L.h),
+                           at(L.dab), dgp, s);
+  else
+    moe::launch_tile_up_pair_bwd(lay, x, row_token, offsets, S, m.d, m.F, m.E, w1, w3, dhp, row_g, at(L.h), at(L.dab),
+                                 dgp, at(L.sink), s);
+  moe::launch_dg_sum(dgp, m.F, S, dg, s);
   moe::launch_router_bwd(dg, token_row, topk_idx, topk_w, m.T, m.E, m.K, dlog, s);
   MOE_TRY(check_launch("moe_backward (dgrad)"));
   // dx = sum_k (w1^T da + w3^T db) + W_g dlogit; dW_g = x^T dlogit

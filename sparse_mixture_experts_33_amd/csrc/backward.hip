@@ -17,29 +17,15 @@
 namespace moe {
 namespace {
 
-__device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
-__device__ inline float dsilu_f(float z) {
-  const float s = 1.0f / (1.0f + expf(-z));
-  return s * (1.0f + z * (1.0f - s));
-}
-
-// Slot k of row r (row_token[r] = t and token_row[t*K + k] = r) and its gate weight.
-__device__ inline float row_gate(const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
-                                 int r, int& t_out) {
-  const int t = row_token[r];
-  float g = 0.0f;
-  for (int k = 0; k < K; ++k)
-    if (token_row[(int64_t)t * K + k] == r) g = topk_w[(int64_t)t * K + k];
-  t_out = t;
-  return g;
-}
-
 // Per token t and slot k (row r = token_row[t][k], gate g_k): dy_perm[r] = bf16(dy[t]),
-// do_perm[r] = bf16(g_k dy[t]). One block per token, so dy[t] is read once for its K rows.
+// do_perm[r] = bf16(g_k dy[t]), row_g[r] = g_k. One block per token, so dy[t] is read once for its K
+// rows.
 __global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict__ dy, const int32_t* __restrict__ token_row,
                                                         const float* __restrict__ topk_w, int K, int d,
-                                                        bf16_t* __restrict__ dy_perm, bf16_t* __restrict__ do_perm) {
+                                                        bf16_t* __restrict__ dy_perm, bf16_t* __restrict__ do_perm,
+                                                        float* __restrict__ row_g) {
   const int64_t t = blockIdx.x;
+  if (threadIdx.x < K) row_g[token_row[t * K + threadIdx.x]] = topk_w[t * K + threadIdx.x];
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(dy + t * d + c);
     const f32x4_t b = *reinterpret_cast<const f32x4_t*>(dy + t * d + c + 4);
@@ -56,48 +42,61 @@ __global__ __launch_bounds__(256) void gather_dy_kernel(const float* __restrict_
   }
 }
 
-// Per row r: from the recomputed pre-activations a = A[r], b = B[r] and dh' = DHP[r] (fp32):
-// h = bf16(silu(a) b) (as the forward stores it), dg[r] = sum_f dh'_f h_f (fixed order),
-// dab[r] = [bf16(da) | bf16(db)] with da = g dh' b silu'(a), db = g dh' silu(a). One block per row.
+// Per row r: from its pre-activations a = A[r], b = B[r] (kept by the forward) and dh' = DHP[r]
+// (fp32): h = bf16(silu(a) b) (as the forward stores it), dab[r] = [bf16(da) | bf16(db)] with
+// da = g dh' b silu'(a), db = g dh' silu(a), and the gate-gradient partials of dg[r] = sum_f dh'_f h_f
+// per 64-column chunk c, to dgp[c * rows + r]. One block per row; thread i takes the 4 columns
+// 4 i + 1024 j, so 16 consecutive lanes hold one chunk: block a = (i / 4) % 4, quad (i % 4). The
+// recomputing path forms the same values in the pre-activation product's epilogue (tile_gemm.hip).
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ A, const float* __restrict__ B,
                                                          const float* __restrict__ DHP,
                                                          const int32_t* __restrict__ row_token,
                                                          const int32_t* __restrict__ token_row,
-                                                         const float* __restrict__ topk_w, int K, int F,
+                                                         const float* __restrict__ topk_w, int K, int F, int64_t rows,
                                                          bf16_t* __restrict__ h, bf16_t* __restrict__ dab,
-                                                         float* __restrict__ dg) {
-  __shared__ float part[256 / kWave];
+                                                         float* __restrict__ dgp) {
   const int r = blockIdx.x;
   int t;
   const float g = row_gate(row_token, token_row, topk_w, K, r, t);
   const int64_t o = (int64_t)r * F;
-  float acc = 0.0f;
+  // F is a multiple of 256, so every wavefront runs the same iterations (the shuffles see whole waves)
   for (int f = threadIdx.x * 4; f < F; f += 256 * 4) {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(A + o + f);
     const f32x4_t b = *reinterpret_cast<const f32x4_t*>(B + o + f);
     const f32x4_t p = *reinterpret_cast<const f32x4_t*>(DHP + o + f);
     float hv[4], da[4], db[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float s = silu_f(a[q]);
-      hv[q] = s * b[q];
-      const float dh = g * p[q];
-      da[q] = dh * b[q] * dsilu_f(a[q]);
-      db[q] = dh * s;
-    }
+    for (int q = 0; q < 4; ++q) swiglu_bwd_elem(a[q], b[q], p[q], g, hv[q], da[q], db[q]);
     const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
     *reinterpret_cast<u32x2_t*>(h + o + f) = u32x2_t{h01, h23};
-    acc = fmaf(p[0], bf16_lo(h01), acc);
-    acc = fmaf(p[1], bf16_hi(h01), acc);
-    acc = fmaf(p[2], bf16_lo(h23), acc);
-    acc = fmaf(p[3], bf16_hi(h23), acc);
     *reinterpret_cast<u32x2_t*>(dab + 2 * o + f) = u32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
     *reinterpret_cast<u32x2_t*>(dab + 2 * o + F + f) = u32x2_t{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+    float v = dg_quad(p, h01, h23);
+    v += __shfl_xor(v, 4, kWave);  // the blocks of the chunk: (a0 + a1) + (a2 + a3)
+    v += __shfl_xor(v, 8, kWave);
+    v += __shfl_xor(v, 1, kWave);  // then the quads
+    v += __shfl_xor(v, 2, kWave);
+    if ((threadIdx.x & 15) == 0) dgp[(int64_t)(f >> 6) * rows + r] = v;
   }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) dg[r] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// dg[r] = sum over the 64-column chunks c of dgp[c * rows + r] (nc a multiple of 4): quarter q of
+// the chunks (nc/4 consecutive ones) summed in order, then (q0 + q1) + (q2 + q3). A block takes 64
+// rows; lane l of a wavefront takes row l % 16 and quarter l / 16.
+__global__ __launch_bounds__(256) void dg_sum_kernel(const float* __restrict__ dgp, int nc, int64_t rows,
+                                                     float* __restrict__ dg) {
+  const int q = (threadIdx.x >> 4) & 3;
+  const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (threadIdx.x & 15);
+  const int nq = nc / 4;
+  float acc = 0.0f;
+  if (r < rows) {
+    const float* p = dgp + (int64_t)q * nq * rows + r;
+#pragma unroll 8
+    for (int c = 0; c < nq; ++c) acc += p[c * rows];
+  }
+  acc += __shfl_xor(acc, 16, kWave);
+  acc += __shfl_xor(acc, 32, kWave);
+  if (r < rows && q == 0) dg[r] = acc;
 }
 
 // Per token: dlogit_{e_k} = g_k (dg_k - sum_j g_j dg_j), zero for the experts not kept.
@@ -246,17 +245,21 @@ __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict
 int dwgate_chunks(int64_t T) { return (int)((T + kDwgChunk - 1) / kDwgChunk); }
 
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
-                      int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t s) {
+                      int64_t rows, int d, void* dy_perm, void* do_perm, float* row_g, hipStream_t s) {
   (void)row_token;
   launch_kernel(gather_dy_kernel, dim3((unsigned)(rows / K)), dim3(256), 0, s, dy, token_row, topk_w, K, d,
-                static_cast<bf16_t*>(dy_perm), static_cast<bf16_t*>(do_perm));
+                static_cast<bf16_t*>(dy_perm), static_cast<bf16_t*>(do_perm), row_g);
 }
 
 void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,
                        const int32_t* token_row, const float* topk_w, int K, int64_t rows, int F, void* h, void* dab,
-                       float* dg, hipStream_t s) {
+                       float* dgp, hipStream_t s) {
   launch_kernel(swiglu_bwd_kernel, dim3((unsigned)rows), dim3(256), 0, s, A, B, DHP, row_token, token_row, topk_w, K,
-                F, static_cast<bf16_t*>(h), static_cast<bf16_t*>(dab), dg);
+                F, rows, static_cast<bf16_t*>(h), static_cast<bf16_t*>(dab), dgp);
+}
+
+void launch_dg_sum(const float* dgp, int F, int64_t rows, float* dg, hipStream_t s) {
+  launch_kernel(dg_sum_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, s, dgp, F / 64, rows, dg);
 }
 
 void launch_router_bwd(const float* dg, const int32_t* token_row, const int32_t* topk_idx, const float* topk_w,

@@ -86,4 +86,47 @@ __device__ inline bool find_tile(const int32_t* offsets, int E, int tile, int id
   return false;
 }
 
+// SwiGLU expert activation (xyznot.com summary, "Método": silu(x w1) * (x w3)) and its derivative.
+__device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
+__device__ inline float dsilu_f(float z) {
+  const float s = 1.0f / (1.0f + expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// Slot k of row r (row_token[r] = t and token_row[t*K + k] = r) and its gate weight.
+__device__ inline float row_gate(const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
+                                 int r, int& t_out) {
+  const int t = row_token[r];
+  float g = 0.0f;
+  for (int k = 0; k < K; ++k)
+    if (token_row[(int64_t)t * K + k] == r) g = topk_w[(int64_t)t * K + k];
+  t_out = t;
+  return g;
+}
+
+// Backward of one SwiGLU element of a routed row with gate g, pre-activations a, b and
+// dh' = (w2^T dy)_f = p: h = silu(a) b, da = g p b silu'(a), db = g p silu(a). The kernel that reads
+// stored pre-activations and the pre-activation product's epilogue both call this, so the two give
+// the same bits.
+__device__ inline void swiglu_bwd_elem(float a, float b, float p, float g, float& h, float& da, float& db) {
+  const float s = silu_f(a);
+  h = s * b;
+  const float dh = g * p;
+  da = dh * b * dsilu_f(a);
+  db = dh * s;
+}
+
+// Gate-gradient partial of 4 consecutive columns: sum over q of p_q h_q in q order, h_q as stored
+// (bf16). The gate gradient of a row is summed in a fixed order from these: the four quads of a
+// 16-column block and the four blocks of a 64-column chunk as two pairwise trees
+// ((q0 + q1) + (q2 + q3) over blocks, then over quads), then the chunks in column order.
+__device__ inline float dg_quad(f32x4_t p, uint32_t h01, uint32_t h23) {
+  float v = 0.0f;
+  v = fmaf(p[0], bf16_lo(h01), v);
+  v = fmaf(p[1], bf16_hi(h01), v);
+  v = fmaf(p[2], bf16_lo(h23), v);
+  v = fmaf(p[3], bf16_hi(h23), v);
+  return v;
+}
+
 }  // namespace moe

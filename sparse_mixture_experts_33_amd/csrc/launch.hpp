@@ -82,6 +82,15 @@ void launch_tile_wt(int layout, const void* act, const int32_t* offsets, int64_t
 void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows,
                          int d, int F, int E, const void* w1, const void* w3, float* a, float* b, hipStream_t stream,
                          void* h = nullptr, bool hpk = false);
+// Backward pass: the same pair product finishing the SwiGLU derivative in its epilogue, given
+// dh' = w2^T dy of every row (fp32 [rows][F]): h = bf16(silu(a) b) [rows][F], dab = [bf16(da) |
+// bf16(db)] [rows][2F] and the gate-gradient partials dgp [F/64][rows] (launch_dg_sum adds them up),
+// the same bits as launch_swiglu_bwd forms from stored a, b. row_token gathers the rows of x, row_g
+// holds each row's gate (launch_gather_dy); sink is 16 bytes of device memory whose contents are
+// never used (it takes the stores of the rows past a tile's end).
+void launch_tile_up_pair_bwd(int layout, const void* act, const int32_t* row_token, const int32_t* offsets,
+                             int64_t rows, int d, int F, int E, const void* w1, const void* w3, const float* dhp,
+                             const float* row_g, void* h, void* dab, float* dgp, void* sink, hipStream_t stream);
 void launch_tile_down(int layout, const void* h, const int32_t* offsets, int64_t rows, int d, int F, int E,
                       const void* w2, float* y_perm, int ksplit, float* y_part, hipStream_t stream, bool hpk = false);
 
@@ -102,13 +111,16 @@ void launch_combine(const float* y_perm, const float* y_part, int nparts, const 
 void launch_rmsnorm(const float* h, int64_t T, int d, float eps, void* x_bf16, hipStream_t stream);
 
 // Backward pass (bf16 operands, fp32 sums; see backward.hip).
-// dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]) for row r = (t, k) with gate g.
+// dy_perm[r] = bf16(dy[t]), do_perm[r] = bf16(g dy[t]), row_g[r] = g for row r = (t, k) with gate g.
 void launch_gather_dy(const float* dy, const int32_t* row_token, const int32_t* token_row, const float* topk_w, int K,
-                      int64_t rows, int d, void* dy_perm, void* do_perm, hipStream_t stream);
-// h = bf16(silu(A) B), dg = dh' . h, dab = [bf16(g dh' B silu'(A)) | bf16(g dh' silu(A))] per row.
+                      int64_t rows, int d, void* dy_perm, void* do_perm, float* row_g, hipStream_t stream);
+// h = bf16(silu(A) B), dab = [bf16(g dh' B silu'(A)) | bf16(g dh' silu(A))] per row, and the partials
+// dgp [F/64][rows] of dg = dh' . h per 64-column chunk (F a multiple of 256).
 void launch_swiglu_bwd(const float* A, const float* B, const float* DHP, const int32_t* row_token,
                        const int32_t* token_row, const float* topk_w, int K, int64_t rows, int F, void* h, void* dab,
-                       float* dg, hipStream_t stream);
+                       float* dgp, hipStream_t stream);
+// dg[r] = sum of the F/64 partials of row r in chunk order.
+void launch_dg_sum(const float* dgp, int F, int64_t rows, float* dg, hipStream_t stream);
 void launch_router_bwd(const float* dg, const int32_t* token_row, const int32_t* topk_idx, const float* topk_w,
                        int64_t T, int E, int K, float* dlogits, hipStream_t stream);
 // dxp rows are rebuilt from nparts extra k-range partials (part, each T*K*d) before the sum.

@@ -63,7 +63,16 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kBT = 320;  // token rows per tile (at most) of the products over token rows
 
-__device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
+// SBWD: what the backward pass's pre-activation product finishes in its epilogue (the SwiGLU
+// derivative), given dh' = w2^T dy of every row (see swiglu_bwd_elem).
+struct SwigluBwdArgs {
+  const float* dhp = nullptr;    // [rows][N] dh' (fp32)
+  const float* row_g = nullptr;  // [rows] the gate of each row
+  int64_t rows = 0;
+  bf16_t* dab = nullptr;  // [rows][2N]: bf16(da) | bf16(db)
+  float* dgp = nullptr;   // [N/64][rows]: gate-gradient partial of each 64-column chunk
+  void* sink = nullptr;   // 16 bytes that take the stores of rows past a tile's end
+};
 
 // WGRAD: weight-gradient mode of the backward pass. Per expert e the product runs over the rows of
 // e's group instead of over a fixed K: out[e][m][n] = sum over the group's rows r of
@@ -87,7 +96,12 @@ __device__ inline float silu_t(float z) { return z / (1.0f + expf(-z)); }
 // group e is packed row hpk_row0(e) + r - offsets[e], hpk_row0(e) = sum over e' < e of the group
 // sizes rounded up to 16. Packed rows past a group's end are never written; the down product reads
 // them with their block, and the output rows they produce are not stored.
-template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT, bool HPK = false>
+// SBWD (backward pass, SWIGLU): instead of storing a = x.w1^T and b = x.w3^T, the epilogue reads dh'
+// at the same elements and stores h = bf16(silu(a) b) to out (row-major [rows][N]), [da | db] and the
+// gate-gradient partials (swiglu_bwd_elem, dg_quad: the lane's four 16-column blocks pairwise, then
+// the four lanes of a row pairwise, one partial per 64-column chunk of a wavefront).
+template <int BW, int BT, bool PACKED, bool SWIGLU, bool WGRAD, bool WT, typename OutT, bool HPK = false,
+          bool SBWD = false>
 __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restrict__ act,
                                                            const int32_t* __restrict__ row_src,
                                                            const int32_t* __restrict__ offsets,
@@ -95,10 +109,11 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ wb, OutT* __restrict__ out,
                                                            int K, int N, int E, int ksplit, float* __restrict__ part,
                                                            int64_t part_stride, int M, int ldw,
-                                                           bf16_t* __restrict__ hout) {
+                                                           bf16_t* __restrict__ hout, SwigluBwdArgs sb) {
   static_assert(!WGRAD || (!SWIGLU && WT), "the weight-gradient mode reads both operands k-major");
   static_assert(!WT || !SWIGLU, "transposed weights: plain product only");
   static_assert(!HPK || (!WT && !WGRAD), "packed h: forward products only");
+  static_assert(!SBWD || (SWIGLU && !HPK && sizeof(OutT) == 2), "SwiGLU derivative: the pair product, h row-major");
   static_assert(BW == 256 && (BT == 256 || (BT == 320 && !WGRAD)), "tiles are 256 x 256, or 256 x 320 but for WGRAD");
   constexpr int NW = SWIGLU ? BW / 2 : BW;  // output columns per tile
   constexpr int AB = BW / 32;               // weight blocks per wavefront
@@ -267,6 +282,15 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
     ntl += (wave + 8 * i < TB && wave + 8 * i < nblk) ? 1 : 0;
   }
   const int nl = 2 + (WGRAD ? 2 : ntl);  // loads per step (uniform over the wavefront)
+  // SBWD: the gates of this lane's epilogue rows, loaded with the row indices (before the k-loop)
+  float sgate[SBWD ? BB : 1];
+  if constexpr (SBWD) {
+#pragma unroll
+    for (int b = 0; b < BB; ++b) {
+      const int tr = (wt + 4 * b) * 16 + (lane & 15);
+      sgate[b] = sb.row_g[r0 + (tr < nrows ? tr : 0)];
+    }
+  }
   const int wl32 = PACKED ? lane * 8 : (lane & 15) * K + (lane >> 4) * 8;
   constexpr int64_t kW32 = PACKED ? 512 : 32;
   const int64_t wrow0 = ((int64_t)e * N + n0) * K;  // forward: first element of the tile's weights
@@ -614,7 +638,53 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   auto hpk_off = [&](int tb, int f) -> int64_t {
     return (((int64_t)(pb0 + tb) * (N / 32) + (f >> 5)) * 64 + li + 16 * ((f & 31) >> 3)) * 8 + (f & 7);
   };
-  if constexpr (SWIGLU && sizeof(OutT) == 4) {
+  if constexpr (SBWD) {
+    // every lane takes part in the shuffles; rows past the tile's end compute on a valid row and
+    // store to the sink (stores without branches, so that the compiler keeps the arithmetic out of
+    // conditional code, where its waits for the loads become waits for everything). The dh' loads run two token blocks ahead: block b + 2's go out after block b's
+    // stores, so the wait for a block's loads never covers the stores of the block just before it
+    // (the wait for a load also waits for every store issued before it).
+    f32x4_t pvs[2][AB / 2];
+    auto load_dhp = [&](int b, f32x4_t* dst) {
+      const int tr = (wt + 4 * b) * 16 + li;
+      const int r = r0 + (tr < nrows ? tr : 0);
+#pragma unroll
+      for (int a = 0; a < AB / 2; ++a)
+        dst[a] = *reinterpret_cast<const f32x4_t*>(sb.dhp + (int64_t)r * N + n0 + (wr * (AB / 2) + a) * 16 + 4 * lg);
+    };
+    load_dhp(0, pvs[0]);
+    if (BB > 1) load_dhp(1, pvs[1]);
+#pragma unroll
+    for (int b = 0; b < BB; ++b) {
+      const int tr = (wt + 4 * b) * 16 + li;
+      const bool ok = tr < nrows;
+      const int r = r0 + (ok ? tr : 0);
+      const float g = sgate[b];
+      float v[AB / 2];
+#pragma unroll
+      for (int a = 0; a < AB / 2; ++a) {
+        const int f = n0 + (wr * (AB / 2) + a) * 16 + 4 * lg;
+        const f32x4_t pv = pvs[b & 1][a];
+        float hv[4], da[4], db[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) swiglu_bwd_elem(acc[a][b][q], acc[a + AB / 2][b][q], pv[q], g, hv[q], da[q], db[q]);
+        const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
+        v[a] = dg_quad(pv, h01, h23);
+        u32x2_t* const sink = static_cast<u32x2_t*>(sb.sink);
+        u32x2_t* const ph = ok ? reinterpret_cast<u32x2_t*>(out + (int64_t)r * N + f) : sink;
+        u32x2_t* const pa = ok ? reinterpret_cast<u32x2_t*>(sb.dab + (int64_t)r * 2 * N + f) : sink;
+        u32x2_t* const pb = ok ? reinterpret_cast<u32x2_t*>(sb.dab + (int64_t)r * 2 * N + N + f) : sink;
+        *ph = u32x2_t{h01, h23};
+        *pa = u32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        *pb = u32x2_t{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+      }
+      float x = (v[0] + v[1]) + (v[2] + v[3]);
+      x += __shfl_xor(x, 16, kWave);  // lanes l, l + 16, l + 32, l + 48 hold the four quads of row li
+      x += __shfl_xor(x, 32, kWave);
+      if (ok && lg == 0) sb.dgp[(int64_t)((n0 >> 6) + wr) * sb.rows + r] = x;
+      if (b + 2 < BB) load_dhp(b + 2, pvs[b & 1]);
+    }
+  } else if constexpr (SWIGLU && sizeof(OutT) == 4) {
     // pre-activation pair (backward pass): a = x.w1^T to out, b = x.w3^T to part, both fp32
 #pragma unroll
     for (int a = 0; a < AB / 2; ++a)
@@ -631,7 +701,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         if (hout) {  // and h = bf16(silu(a) b), as the fused epilogue below forms it
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_t(acc[a][b][q]) * v[q];
+          for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[a][b][q]) * v[q];
           const int64_t oh = HPK ? hpk_off(wt + 4 * b, n0 + (wr * (AB / 2) + a) * 16 + 4 * lg) : o;
           *reinterpret_cast<u32x2_t*>(hout + oh) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
         }
@@ -646,7 +716,7 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
         const int f = n0 + (wr * (AB / 2) + a) * 16 + 4 * lg;
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = silu_t(acc[a][b][q]) * acc[a + AB / 2][b][q];
+        for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[a][b][q]) * acc[a + AB / 2][b][q];
         *reinterpret_cast<u32x2_t*>(out + (HPK ? hpk_off(wt + 4 * b, f) : (int64_t)(r0 + tr) * N + f)) =
             u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
@@ -671,17 +741,18 @@ __global__ __launch_bounds__(512, 1) void tile_gemm_kernel(const bf16_t* __restr
   }
 }
 
-template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false, bool HPK = false>
+template <int BW, int BT, bool PACKED, bool SWIGLU, typename OutT, bool WT = false, bool HPK = false,
+          bool SBWD = false>
 void launch_tile(const void* act, const int32_t* row_src, const int32_t* offsets, int64_t rows, int E, const void* wa,
                  const void* wb, void* out, int K, int N, int ksplit, float* part, hipStream_t s,
-                 void* hout = nullptr) {
+                 void* hout = nullptr, const SwigluBwdArgs& sb = SwigluBwdArgs{}) {
   constexpr int NW = SWIGLU ? BW / 2 : BW;
   const int64_t max_tiles = ((rows + BT - 1) / BT + E) * (N / NW) * ksplit;
   const int64_t grid = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT, HPK>), dim3((unsigned)grid), dim3(512), 0, s,
-                static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
+  launch_kernel((tile_gemm_kernel<BW, BT, PACKED, SWIGLU, false, WT, OutT, HPK, SBWD>), dim3((unsigned)grid),
+                dim3(512), 0, s, static_cast<const bf16_t*>(act), row_src, offsets, static_cast<const bf16_t*>(wa),
                 static_cast<const bf16_t*>(wb), static_cast<OutT*>(out), K, N, E, ksplit, part, rows * N, 0, N,
-                static_cast<bf16_t*>(hout));
+                static_cast<bf16_t*>(hout), sb);
 }
 
 }  // namespace
@@ -725,7 +796,7 @@ void launch_tile_wgrad(const void* p, int M, int ldp, const void* q, int N, int 
     launch_kernel(kernel, dim3((unsigned)grid), dim3(512), 0, s, static_cast<const bf16_t*>(p),
                   static_cast<const int32_t*>(nullptr), offsets, static_cast<const bf16_t*>(q),
                   static_cast<const bf16_t*>(nullptr), out, ldp, N, E, 1, static_cast<float*>(nullptr), (int64_t)0, M,
-                  ldq, static_cast<bf16_t*>(nullptr));
+                  ldq, static_cast<bf16_t*>(nullptr), SwigluBwdArgs{});
   };
   if (packed_out)
     go(tile_gemm_kernel<256, 256, true, false, true, true, float>);
@@ -757,6 +828,24 @@ void launch_tile_up_pair(int layout, const void* act, const int32_t* row_src, co
     launch_tile<256, kBT, false, true, float, false, true>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
   else
     launch_tile<256, kBT, false, true, float>(act, row_src, offsets, rows, E, w1, w3, a, d, F, 1, b, s, h);
+}
+
+void launch_tile_up_pair_bwd(int layout, const void* act, const int32_t* row_token, const int32_t* offsets,
+                             int64_t rows, int d, int F, int E, const void* w1, const void* w3, const float* dhp,
+                             const float* row_g, void* h, void* dab, float* dgp, void* sink, hipStream_t s) {
+  SwigluBwdArgs sb;
+  sb.dhp = dhp;
+  sb.row_g = row_g;
+  sb.rows = rows;
+  sb.dab = static_cast<bf16_t*>(dab);
+  sb.dgp = dgp;
+  sb.sink = sink;
+  if (layout == kPacked)
+    launch_tile<256, kBT, true, true, bf16_t, false, false, true>(act, row_token, offsets, rows, E, w1, w3, h, d, F, 1,
+                                                                  nullptr, s, nullptr, sb);
+  else
+    launch_tile<256, kBT, false, true, bf16_t, false, false, true>(act, row_token, offsets, rows, E, w1, w3, h, d, F, 1,
+                                                                   nullptr, s, nullptr, sb);
 }
 
 void launch_tile_wt(int layout, const void* act, const int32_t* offsets, int64_t rows, int N, int K, int E,
