@@ -344,6 +344,8 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(const bf16_t* __restr
 }
 
 // h[t] += a[t] (fp32), then x[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps)); one wavefront per row.
+// Rows of up to kResNormRegD values stay in registers between the two.
+constexpr int kResNormRegD = 4096;
 __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ h, const float* __restrict__ a,
                                                             int64_t T, int d, float eps, bf16_t* __restrict__ x) {
   const int lane = threadIdx.x & 63;
@@ -352,22 +354,47 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(float* __restrict__ 
   float* row = h + t * d;
   const float* add = a + t * d;
   float ss = 0.0f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
+  auto sum_in = [&](int c) {
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
     v += *reinterpret_cast<const f32x4_t*>(add + c);
     *reinterpret_cast<f32x4_t*>(row + c) = v;
+    return v;
+  };
+  auto sq = [&](const f32x4_t& v) {
     ss = fmaf(v[0], v[0], ss);
     ss = fmaf(v[1], v[1], ss);
     ss = fmaf(v[2], v[2], ss);
     ss = fmaf(v[3], v[3], ss);
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+  };
+  auto put = [&](int c, const f32x4_t& v, float inv) {
     *reinterpret_cast<u32x2_t*>(x + t * d + c) = u32x2_t{pack_bf16x2(v[0] * inv, v[1] * inv),
                                                          pack_bf16x2(v[2] * inv, v[3] * inv)};
+  };
+  if (d <= kResNormRegD) {
+    // the updated row stays in registers for the scaling (h is read once)
+    constexpr int kPer = kResNormRegD / (kWave * 4);
+    f32x4_t v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * 4 + kWave * 4 * i;
+      if (c < d) {
+        v[i] = sum_in(c);
+        sq(v[i]);
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * 4 + kWave * 4 * i;
+      if (c < d) put(c, v[i], inv);
+    }
+    return;
   }
+  for (int c = lane * 4; c < d; c += kWave * 4) sq(sum_in(c));
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane * 4; c < d; c += kWave * 4) put(c, *reinterpret_cast<const f32x4_t*>(row + c), inv);
 }
 
 __global__ void set_offsets_kernel(int32_t* off, int32_t T) {

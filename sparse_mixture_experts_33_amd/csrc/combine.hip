@@ -79,6 +79,10 @@ void launch_mode(const float* y_perm, const float* y_part, int nparts, const int
   }
 }
 
+// One wavefront per token; rows of up to kNormRegD values are held in registers between the sum
+// of squares and the scaling. The sum runs over a lane's slices in ascending order, then the
+// butterfly, whatever the path.
+constexpr int kNormRegD = 4096;
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int64_t T, int d, float eps,
                                                       bf16_t* __restrict__ x) {
   const int lane = threadIdx.x & 63;
@@ -86,20 +90,41 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   if (t >= T) return;
   const float* row = h + t * d;
   float ss = 0.0f;
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+  auto sq = [&](const f32x4_t& v) {
     ss = fmaf(v[0], v[0], ss);
     ss = fmaf(v[1], v[1], ss);
     ss = fmaf(v[2], v[2], ss);
     ss = fmaf(v[3], v[3], ss);
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane * 4; c < d; c += kWave * 4) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
+  };
+  auto put = [&](int c, const f32x4_t& v, float inv) {
     *reinterpret_cast<u32x2_t*>(x + t * d + c) = u32x2_t{pack_bf16x2(v[0] * inv, v[1] * inv),
                                                          pack_bf16x2(v[2] * inv, v[3] * inv)};
+  };
+  if (d <= kNormRegD) {
+    // the row in registers: one read of h, all of a lane's loads in flight together
+    constexpr int kPer = kNormRegD / (kWave * 4);
+    f32x4_t v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * 4 + kWave * 4 * i;
+      v[i] = c < d ? *reinterpret_cast<const f32x4_t*>(row + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane * 4 + kWave * 4 * i < d) sq(v[i]);
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * 4 + kWave * 4 * i;
+      if (c < d) put(c, v[i], inv);
+    }
+    return;
   }
+  for (int c = lane * 4; c < d; c += kWave * 4) sq(*reinterpret_cast<const f32x4_t*>(row + c));
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane * 4; c < d; c += kWave * 4) put(c, *reinterpret_cast<const f32x4_t*>(row + c), inv);
 }
 
 }  // namespace

@@ -172,7 +172,22 @@ __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict
                                                         float* __restrict__ logits) {
   __shared__ u32x4_t wl[kRouteLdsMaxD];
   const int d8 = d / 8;
-  for (int r = threadIdx.x; r < d; r += blockDim.x) wl[(r & 7) * d8 + (r >> 3)] = load16(wg + (int64_t)r * 8);
+  {
+    // all of a thread's W_g loads in flight together (a loop that stores each load before the
+    // next one is issued waits out one L2 round trip per row slice)
+    constexpr int kPer = kRouteLdsMaxD / 256;
+    u32x4_t tmp[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = threadIdx.x + 256 * i;
+      if (r < d) tmp[i] = load16(wg + (int64_t)r * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = threadIdx.x + 256 * i;
+      if (r < d) wl[(r & 7) * d8 + (r >> 3)] = tmp[i];
+    }
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
