@@ -174,32 +174,56 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, 
 }
 
 // dW_g partials: chunk c of kDwgChunk tokens, part[c][j][e] = sum over its tokens t (ascending) of
-// x[t][j] * dlogit[t][e]. A thread takes C consecutive columns (8 with up to 8 experts: one 16-byte
-// load per token; 2 beyond) and its token loop is unrolled so that several loads are in flight; the
+// x[t][j] * dlogit[t][e]. A thread takes C consecutive columns (4 with up to 8 experts: one 8-byte
+// load per token; 2 beyond) and its token loop is unrolled so that U loads are in flight; the
 // chunks' partials are then added in chunk order by dwgate_sum_kernel.
 constexpr int kDwgChunk = 64;
-template <int EMAX, int C>
+// EXACT: E == EMAX, so the expert loops carry no bound test (with one, every expert of every token
+// became a branch and a wait for its LDS read).
+template <int EMAX, int C, bool EXACT>
 __global__ __launch_bounds__(64) void dwgate_part_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dlogits,
-                                                         int64_t T, int d, int E, float* __restrict__ part) {
-  static_assert(C == 8 || C == 2, "columns per thread");
+                                                         int64_t T, int d, int E_, float* __restrict__ part) {
+  static_assert(C == 4 || C == 2, "columns per thread");
+  const int E = EXACT ? EMAX : E_;
   const int j0 = (blockIdx.x * 64 + threadIdx.x) * C;
   const int ch = blockIdx.y;
+  // the chunk's logit gradients, staged once (per token, every lane needs the same E values)
+  __shared__ __attribute__((aligned(16))) float sdl[kDwgChunk * EMAX];
+  const int64_t t0 = (int64_t)ch * kDwgChunk, t1 = min<int64_t>(T, t0 + kDwgChunk);
+  if constexpr (EXACT) {
+    // 16-byte pieces, all of a thread's loads in flight together
+    constexpr int kPer = kDwgChunk * EMAX / 4 / 64;
+    const int n16 = (int)(t1 - t0) * EMAX / 4;
+    f32x4_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + 64 * k;
+      if (i < n16) v[k] = reinterpret_cast<const f32x4_t*>(dlogits + t0 * EMAX)[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + 64 * k;
+      if (i < n16) reinterpret_cast<f32x4_t*>(sdl)[i] = v[k];
+    }
+  } else {
+    for (int i = threadIdx.x; i < (int)(t1 - t0) * E; i += 64) sdl[i] = dlogits[t0 * E + i];
+  }
+  __syncthreads();
   if (j0 >= d) return;
   float acc[C][EMAX];
 #pragma unroll
   for (int c = 0; c < C; ++c)
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) acc[c][e] = 0.0f;
-  const int64_t t0 = (int64_t)ch * kDwgChunk, t1 = min<int64_t>(T, t0 + kDwgChunk);
-  constexpr int U = 8;  // tokens whose loads are issued together
+  constexpr int U = 16;  // tokens whose loads are issued together
   for (int64_t tb = t0; tb < t1; tb += U) {
     uint32_t xv[U][C / 2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if constexpr (C == 8) {
-        const u32x4_t v = tb + u < t1 ? load16(x + (tb + u) * d + j0) : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[u][q] = v[q];
+      if constexpr (C == 4) {
+        const u32x2_t v = tb + u < t1 ? *reinterpret_cast<const u32x2_t*>(x + (tb + u) * d + j0) : u32x2_t{0u, 0u};
+        xv[u][0] = v[0];
+        xv[u][1] = v[1];
       } else {
         xv[u][0] = tb + u < t1 ? *reinterpret_cast<const uint32_t*>(x + (tb + u) * d + j0) : 0u;
       }
@@ -207,7 +231,7 @@ __global__ __launch_bounds__(64) void dwgate_part_kernel(const bf16_t* __restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (tb + u >= t1) break;
-      const float* dl = dlogits + (tb + u) * E;
+      const float* dl = sdl + (tb + u - t0) * E;
       float xf[C];
 #pragma unroll
       for (int q = 0; q < C / 2; ++q) {
@@ -236,7 +260,8 @@ __global__ __launch_bounds__(256) void dwgate_sum_kernel(const float* __restrict
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)d * E) return;
   float s = 0.0f;
-  for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * d * E + i];
+#pragma unroll 16
+  for (int ch = 0; ch < nch; ++ch) s += part[(int64_t)ch * d * E + i];  // loads in flight together, sums in order
   dwg[i] = s;
 }
 
@@ -283,11 +308,14 @@ void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* t
 void launch_dwgate(const void* x, const float* dlogits, int64_t T, int d, int E, float* part, float* dwg, hipStream_t s) {
   const int nch = dwgate_chunks(T);
   const bf16_t* xb = static_cast<const bf16_t*>(x);
-  if (E <= 8)
-    launch_kernel(dwgate_part_kernel<8, 8>, dim3((unsigned)((d + 511) / 512), (unsigned)nch), dim3(64), 0, s, xb,
-                  dlogits, T, d, E, part);
+  if (E == 8)
+    launch_kernel(dwgate_part_kernel<8, 4, true>, dim3((unsigned)((d + 255) / 256), (unsigned)nch), dim3(64), 0, s,
+                  xb, dlogits, T, d, E, part);
+  else if (E < 8)
+    launch_kernel(dwgate_part_kernel<8, 4, false>, dim3((unsigned)((d + 255) / 256), (unsigned)nch), dim3(64), 0, s,
+                  xb, dlogits, T, d, E, part);
   else
-    launch_kernel(dwgate_part_kernel<kMaxExperts, 2>, dim3((unsigned)((d + 127) / 128), (unsigned)nch), dim3(64), 0, s,
+    launch_kernel(dwgate_part_kernel<kMaxExperts, 2, false>, dim3((unsigned)((d + 127) / 128), (unsigned)nch), dim3(64), 0, s,
                   xb, dlogits, T, d, E, part);
   launch_kernel(dwgate_sum_kernel, dim3((unsigned)(((int64_t)d * E + 255) / 256)), dim3(256), 0, s, part, nch, d, E, dwg);
 }
