@@ -769,8 +769,10 @@ int tile_down_ksplit(int dtype, int64_t rows, int E, int d, int F) {
   // each round into 1/ks of a round; every extra range costs one more fp32 partial written and
   // read back (8*rows*d bytes at ~6.5 TB/s), expressed in tile times (a 256 x 256 x F tile at
   // ~4 TFLOP/s per CU), plus a fixed 0.2 tile times (the fill and drain of each range's k-loop
-  // and output; fitted to step times measured with the split forced to 1..4: prefill T = 4096
-  // is fastest at 2, the skewed T = 16384 layer at 1, the T = 2048 stack within 0.5% at 2..4).
+  // and output; fitted to step times measured with the split forced to 1..4 on 256-row token
+  // tiles: prefill T = 4096 was fastest at 2, the skewed T = 16384 layer at 1, the T = 2048 stack
+  // within 0.5% at 2..4). With 320-row tiles the prefill and T = 2048 shapes fill whole rounds and
+  // take no split.
   // The split depends on the sizes only, so the workspace size does too.
   const double per_e = (double)rows / E;
   const double tiles = (double)E * std::ceil(per_e / kBT) * (d / 256);
