@@ -17,7 +17,10 @@ import hashlib
 import json
 import os
 import re
+import signal
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +50,9 @@ def parse():
     p.add_argument("--pass", dest="pass_", choices=["forward", "backward", "train", "block"], default="forward",
                    help="time moe_forward (default), moe_backward (gradients of the layer) or moe_block_forward "
                         "(decoder block: attention and the layer; workloads block_T*)")
+    p.add_argument("--power", action="store_true",
+                   help="forward pass: also report socket power and graphics clock (amd-smi) over the timed "
+                        "steps; needs a timed region of a few seconds (many --steps)")
     p.add_argument("--weight-layout", choices=["packed", "rowmajor"], default="packed",
                    help="backward and train passes: expert weights (and the weight gradients) fragment-packed "
                         "(default) or row-major")
@@ -135,13 +141,15 @@ def main():
         return
 
     w = mi.WORKLOADS[args.workload]
+    # started before this process touches the GPU: the sampler is a child shell
+    sampler = PowerSampler() if args.power and args.pass_ == "forward" else None
     if args.pass_ in ("backward", "train"):
         backward_bench(args, w, train=args.pass_ == "train")
         return
     if args.pass_ == "block":
         block_bench(args, w)
         return
-    out, ctx = forward_bench(w, args.steps, args.warmup)
+    out, ctx = forward_bench(w, args.steps, args.warmup, sampler)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ctx["x_host"], ctx["host_layer0"], args.cpu_seconds)
     del ctx
@@ -162,9 +170,69 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def forward_bench(w, steps, warmup):
+class PowerSampler:
+    """Socket power and graphics clock over the timed steps, read with `amd-smi metric -p -c` about
+    four times a second by a child shell (in its own process group) that runs from construction
+    until summary(); rocm-smi gives the power cap once at its start."""
+
+    CMD = ("rocm-smi --showmaxpower 2>/dev/null | grep -i 'max graphics package power'; "
+           "while :; do echo \"T $(date +%s.%N)\"; amd-smi metric -p -c 2>/dev/null; sleep 0.2; done")
+
+    def __init__(self):
+        self.f = tempfile.NamedTemporaryFile("w+", prefix="moe_power_", suffix=".txt", delete=False)
+        self.p = subprocess.Popen(["bash", "-c", self.CMD], stdout=self.f, stderr=subprocess.DEVNULL,
+                                  start_new_session=True)
+
+    def summary(self, t0, t1):
+        os.killpg(self.p.pid, signal.SIGTERM)
+        self.p.wait()
+        self.f.close()
+        text = open(self.f.name).read()
+        os.unlink(self.f.name)
+        return parse_power(text, t0, t1)
+
+
+def parse_power(text, t0, t1):
+    """Summary of the PowerSampler log `text` (blocks of amd-smi output, each after a line
+    `T <unix time>`) over the samples taken inside the wall-clock interval [t0, t1]."""
+    cap = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", text)
+    samples, cur, sec = [], None, ""
+    for line in text.splitlines():
+        t = line.strip()
+        if t.startswith("T "):
+            cur = {"t": float(t[2:]), "w": None, "mhz": []}
+            samples.append(cur)
+        elif cur is None:
+            continue
+        elif t.endswith(":") and " " not in t:
+            sec = t[:-1]
+        elif t.startswith("SOCKET_POWER:"):
+            m = re.search(r"([0-9.]+)\s*W", t)
+            cur["w"] = float(m.group(1)) if m else None
+        elif t.startswith("CLK:") and sec.startswith("GFX_"):
+            m = re.search(r"([0-9.]+)\s*MHz", t)
+            if m:
+                cur["mhz"].append(float(m.group(1)))
+    # samples taken inside the timed steps; the readings are averages over about the last second,
+    # so the first second of the timed steps is skipped
+    inside = [x for x in samples if t0 + 1.0 <= x["t"] <= t1 - 0.5 and x["w"] is not None and x["mhz"]]
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2] if v else None
+    ws = [x["w"] for x in inside]
+    clk = [sum(x["mhz"]) / len(x["mhz"]) for x in inside]
+    return {"socket_w_median": med(ws), "socket_w_min": min(ws) if ws else None,
+            "socket_w_max": max(ws) if ws else None, "gfx_mhz_median": med(clk),
+            "gfx_mhz_min": min(clk) if clk else None, "gfx_mhz_max": max(clk) if clk else None,
+            "power_cap_w": float(cap.group(1)) if cap else None, "samples": len(inside),
+            "timed_s": round(t1 - t0, 2), "source": "amd-smi metric -p -c (socket power, mean of the GFX clocks)"}
+
+
+def forward_bench(w, steps, warmup, sampler=None):
     """One step = one moe_forward over the workload's batch (all layers of a stack), inputs resident
-    in HBM, fragment-packed weights. Returns (the bench record without cpu_baseline, host context)."""
+    in HBM, fragment-packed weights. Returns (the bench record without cpu_baseline, host context).
+    With a PowerSampler, the record also carries socket power and graphics clock over the timed steps."""
     import numpy as np
     import torch
 
@@ -257,11 +325,13 @@ def forward_bench(w, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0_wall = time.time()
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev_arrays.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    t1_wall = time.time()
 
     ms_step = elapsed * 1e3 / steps
     tokens_s = w.T * steps / elapsed
@@ -318,6 +388,8 @@ def forward_bench(w, steps, warmup):
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if sampler is not None:
+        out["power"] = sampler.summary(t0_wall, t1_wall)
     return out, {"x_host": x_host, "host_layer0": host_layer0, "layers": layers}
 
 

@@ -16,6 +16,14 @@
 namespace moe {
 namespace {
 
+// a.lo * b.lo + a.hi * b.hi + c for two bf16 pairs (low half first), fp32 accumulation. The
+// pairs are taken by value: a bit cast of a vector element in place reads the vector's first
+// element whatever the index.
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 template <typename T, int V>
 __device__ inline void unpack16(u32x4_t r, float (&v)[V]);
 
@@ -159,53 +167,79 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
     if (lane == tt && t0 + tt < ntok) finalize_token<EMAX>(acc[tt], t0 + tt, E, K, bias, topk_idx, topk_w, logits);
 }
 
-// Many tokens, bf16, E = 8, d <= 4096: W_g (d rows of 16 bytes) is staged in LDS once per
-// workgroup and each wavefront then takes tokens in turn, so W_g is read from L2 once per
-// workgroup rather than once per token. Row r sits at slot (r % 8) * (d / 8) + r / 8: the 64
-// lanes, reading rows 8 l + j of their 16-byte x slices, hit consecutive slots. The accumulation
-// order is that of route_kernel (lane slices k0 = 8 l + 512 i, j ascending, then the butterfly),
-// so the logits are bit-identical to it.
+// Many tokens, bf16, E = 8, d <= 4096: W_g is staged in LDS once per workgroup and each wavefront
+// then takes tokens in turn, so W_g is read from L2 once per workgroup rather than once per token.
+// The products run on the packed bf16 dot instruction (two products and the accumulator per
+// instruction, fp32 accumulation), which takes x and W_g as they are, two consecutive k per dword:
+// x's 16-byte slices already are, and the staging regroups W_g into pairs of rows, the dword of
+// expert e in pair q holding (W_g[2q][e], W_g[2q+1][e]). Experts 0-3 of pair q sit in the 16-byte
+// slot (q % 4) * (d / 8) + q / 4 and experts 4-7 d / 2 slots further, so the 64 lanes, each on 8
+// consecutive k, read consecutive slots. Against converting every W_g value to fp32 for an fma
+// (four times the vector instructions) this takes 16 instead of 27 us at T = 4096. Issuing all eight
+// x slices of a token before its products, or also the next token's, measured slower (20 and 22 us).
 constexpr int kRouteLdsMaxD = 4096;
 __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                                         const float* __restrict__ bias, int64_t ntok, int d, int K,
                                                         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                         float* __restrict__ logits) {
   __shared__ u32x4_t wl[kRouteLdsMaxD];
-  const int d8 = d / 8;
+  const int d8 = d / 8, d2 = d / 2;
   {
     // all of a thread's W_g loads in flight together (a loop that stores each load before the
-    // next one is issued waits out one L2 round trip per row slice)
-    constexpr int kPer = kRouteLdsMaxD / 256;
-    u32x4_t tmp[kPer];
+    // next one is issued waits out one L2 round trip per row pair)
+    constexpr int kPer = kRouteLdsMaxD / 2 / 256;
+    u32x4_t r0[kPer], r1[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int r = threadIdx.x + 256 * i;
-      if (r < d) tmp[i] = load16(wg + (int64_t)r * 8);
+      const int q = threadIdx.x + 256 * i;
+      if (q < d2) {
+        r0[i] = load16(wg + (int64_t)q * 16);
+        r1[i] = load16(wg + (int64_t)q * 16 + 8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int r = threadIdx.x + 256 * i;
-      if (r < d) wl[(r & 7) * d8 + (r >> 3)] = tmp[i];
+      const int q = threadIdx.x + 256 * i;
+      if (q < d2) {
+        // dword c of a row holds experts 2c (low half) and 2c + 1
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          lo[2 * c] = (r0[i][c] & 0xFFFFu) | (r1[i][c] << 16);
+          lo[2 * c + 1] = (r0[i][c] >> 16) | (r1[i][c] & 0xFFFF0000u);
+          hi[2 * c] = (r0[i][c + 2] & 0xFFFFu) | (r1[i][c + 2] << 16);
+          hi[2 * c + 1] = (r0[i][c + 2] >> 16) | (r1[i][c + 2] & 0xFFFF0000u);
+        }
+        const int slot = (q & 3) * d8 + (q >> 2);
+        wl[slot] = lo;
+        wl[d2 + slot] = hi;
+      }
     }
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  // A token's x slices (lane l: k0 = 8 l + 512 i) are all loaded before its products, and the next
+  // token's while they run: a loop that waits for each slice before the next load pays a memory
+  // round trip per slice. Slices past d (and tokens past the end) load valid addresses; such slices
+  // are zeroed and read W_g's last slot, so they add exact zeros (the loads stay unconditional, which
+  // lets the compiler count them instead of waiting for all).
   for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < ntok; t += waves) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll 8
     for (int k0 = lane * 8; k0 < d; k0 += kWave * 8) {
-      float xv[8];
-      unpack16<bf16_t, 8>(load16(x + t * d + k0), xv);
-      const int r0 = k0 >> 3;
+      const u32x4_t xv = load16(x + t * d + k0);
+      const int qb = k0 >> 3;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float w[8];
-        unpack16<bf16_t, 8>(wl[j * d8 + r0], w);
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t lo = wl[j * d8 + qb], hi = wl[d2 + j * d8 + qb];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv[j], w[e], acc[e]);
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = dot2_bf16(xv[j], lo[e], acc[e]);
+          acc[e + 4] = dot2_bf16(xv[j], hi[e], acc[e + 4]);
+        }
       }
     }
 #pragma unroll
@@ -216,8 +250,11 @@ __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict
 
 // Few tokens (decode): one workgroup per token, so all loads of a token are in flight at once.
 // Each of the 256 threads covers 16-byte slices of d; partial sums are reduced across each wave
-// (butterfly) and then across the 4 waves in LDS, in a fixed order.
-template <typename T, int EMAX>
+// (butterfly) and then across the 4 waves in LDS, in a fixed order. VEC (bf16, E = 8): a W_g row is
+// one 16-byte load, and a chunk's slices and rows are all loaded before its products (rows past d
+// load a valid row and meet a zeroed x slice, adding exact zeros), so the loads overlap instead of
+// each waiting out a memory round trip.
+template <typename T, int EMAX, bool VEC>
 __global__ __launch_bounds__(256) void route_token_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                           const float* __restrict__ bias, int64_t ntok, int d,
                                                           int E, int K, int32_t* __restrict__ topk_idx,
@@ -229,16 +266,46 @@ __global__ __launch_bounds__(256) void route_token_kernel(const T* __restrict__ 
   float acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
+  if constexpr (VEC) {
+    static_assert(V == 8 && EMAX == 8, "bf16 rows of 8 experts");
+    constexpr int C = 2;  // slices per thread and chunk (d = 4096 is one chunk)
+    for (int kc = threadIdx.x * 8; kc < d; kc += 256 * 8 * C) {
+      u32x4_t xr[C], wr[C][8];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int k0 = kc + 256 * 8 * c;
+        const int ks = k0 < d ? k0 : d - 8;
+        xr[c] = load16(x + t * d + ks);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wr[c][j] = load16(wg + (int64_t)(ks + j) * 8);
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float xv[8];
+        unpack16<bf16_t, 8>(xr[c], xv);
+        const bool in = kc + 256 * 8 * c < d;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float w[8];
+          unpack16<bf16_t, 8>(wr[c][j], w);
+          const float xj = in ? xv[j] : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(xj, w[e], acc[e]);
+        }
+      }
+    }
+  } else {
 #pragma unroll 4
-  for (int k0 = threadIdx.x * V; k0 < d; k0 += 256 * V) {
-    float xv[V];
-    unpack16<T, V>(load16(x + t * d + k0), xv);
+    for (int k0 = threadIdx.x * V; k0 < d; k0 += 256 * V) {
+      float xv[V];
+      unpack16<T, V>(load16(x + t * d + k0), xv);
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      float w[EMAX];
-      load_gate_row<T, EMAX>(wg + (int64_t)(k0 + j) * E, E, w);
+      for (int j = 0; j < V; ++j) {
+        float w[EMAX];
+        load_gate_row<T, EMAX>(wg + (int64_t)(k0 + j) * E, E, w);
 #pragma unroll
-      for (int e = 0; e < EMAX; ++e) acc[e] = fmaf(xv[j], w[e], acc[e]);
+        for (int e = 0; e < EMAX; ++e) acc[e] = fmaf(xv[j], w[e], acc[e]);
+      }
     }
   }
 #pragma unroll
@@ -269,8 +336,12 @@ template <typename T>
 void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int d, int E, int K, int32_t* idx,
               float* w, float* logits, hipStream_t s) {
   if (T_ <= 512 && E <= 8) {
-    launch_kernel((route_token_kernel<T, 8>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
-                       static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
+    if (sizeof(T) == 2 && E == 8)
+      launch_kernel((route_token_kernel<T, 8, sizeof(T) == 2>), dim3((unsigned)T_), dim3(256), 0, s,
+                    static_cast<const T*>(x), static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
+    else
+      launch_kernel((route_token_kernel<T, 8, false>), dim3((unsigned)T_), dim3(256), 0, s, static_cast<const T*>(x),
+                    static_cast<const T*>(wg), bias, T_, d, E, K, idx, w, logits);
     return;
   }
   if constexpr (sizeof(T) == 2) {

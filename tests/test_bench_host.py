@@ -50,3 +50,29 @@ def test_committed_summaries_name_existing_sources():
             for src in f.group(1).split():
                 assert os.path.exists(os.path.join(csrc, src)), (name, src)
             assert re.search(r"source_digest:\s*[0-9a-f]{16}\b", txt), name
+
+
+def _smi_block(watts, mhz):
+    gfx = "".join(f"        GFX_{i}:\n            CLK: {mhz + i} MHz\n            MIN_CLK: 500 MHz\n"
+                  f"            MAX_CLK: 2400 MHz\n" for i in range(8))
+    return (f"GPU: 0\n    POWER:\n        SOCKET_POWER: {watts} W\n        GFX_VOLTAGE: N/A\n    CLOCK:\n{gfx}"
+            "        MEM_0:\n            CLK: 2000 MHz\n            MIN_CLK: 2000 MHz\n")
+
+
+def test_parse_power_keeps_samples_inside_the_timed_steps():
+    text = ("GPU[0]\t\t: Max Graphics Package Power (W): 1400.0\n"
+            + "T 100.0\n" + _smi_block(250, 150)      # in the first second of the timed steps: dropped
+            + "T 101.0\n" + _smi_block(1390, 2190)
+            + "T 102.0\n" + _smi_block(1400, 2200)
+            + "T 103.0\n" + _smi_block(1398, 2210)
+            + "T 104.9\n" + _smi_block(300, 160))     # during the last half second: dropped
+    p = bench.parse_power(text, 100.0, 105.0)
+    assert p["samples"] == 3 and p["power_cap_w"] == 1400.0
+    assert p["socket_w_median"] == 1398 and p["socket_w_min"] == 1390 and p["socket_w_max"] == 1400
+    # the clock of a sample is the mean over the eight GFX domains (MEM_0's clock is not one of them)
+    assert p["gfx_mhz_median"] == 2203.5 and p["gfx_mhz_min"] == 2193.5
+
+
+def test_parse_power_without_samples():
+    p = bench.parse_power("", 0.0, 10.0)
+    assert p["samples"] == 0 and p["socket_w_median"] is None and p["power_cap_w"] is None
