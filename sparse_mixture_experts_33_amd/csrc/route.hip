@@ -178,6 +178,7 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ x, con
 // (four times the vector instructions) this takes 16 instead of 27 us at T = 4096. Issuing all eight
 // x slices of a token before its products, or also the next token's, measured slower (20 and 22 us).
 constexpr int kRouteLdsMaxD = 4096;
+template <int TPW>
 __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                                         const float* __restrict__ bias, int64_t ntok, int d, int K,
                                                         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -224,27 +225,46 @@ __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict
   // round trip per slice. Slices past d (and tokens past the end) load valid addresses; such slices
   // are zeroed and read W_g's last slot, so they add exact zeros (the loads stay unconditional, which
   // lets the compiler count them instead of waiting for all).
-  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; t < ntok; t += waves) {
-    float acc[8];
+  // TPW consecutive tokens per pass over W_g, so that each LDS read serves TPW tokens; a token's
+  // products keep the order of the single-token pass (tokens past the end compute on the last one
+  // and are not stored)
+  for (int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * TPW; t0 < ntok;
+       t0 += waves * TPW) {
+    const bf16_t* xr[TPW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int u = 0; u < TPW; ++u) xr[u] = x + (t0 + u < ntok ? t0 + u : ntok - 1) * d;
+    float acc[TPW][8];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
 #pragma unroll 8
     for (int k0 = lane * 8; k0 < d; k0 += kWave * 8) {
-      const u32x4_t xv = load16(x + t * d + k0);
+      u32x4_t xv[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) xv[u] = load16(xr[u] + k0);
       const int qb = k0 >> 3;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4_t lo = wl[j * d8 + qb], hi = wl[d2 + j * d8 + qb];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] = dot2_bf16(xv[j], lo[e], acc[e]);
-          acc[e + 4] = dot2_bf16(xv[j], hi[e], acc[e + 4]);
-        }
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[u][e] = dot2_bf16(xv[u][j], lo[e], acc[u][e]);
+            acc[u][e + 4] = dot2_bf16(xv[u][j], hi[e], acc[u][e + 4]);
+          }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = wave_sum(acc[e]);
-    if (lane == 0) finalize_token<8>(acc, t, 8, K, bias, topk_idx, topk_w, logits);
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = wave_sum(acc[u][e]);
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        if (t0 + u < ntok) finalize_token<8>(acc[u], t0 + u, 8, K, bias, topk_idx, topk_w, logits);
+    }
   }
 }
 
@@ -346,10 +366,19 @@ void launch_t(const void* x, const void* wg, const float* bias, int64_t T_, int 
   }
   if constexpr (sizeof(T) == 2) {
     if (E == 8 && d <= kRouteLdsMaxD) {
-      // two workgroups per CU (64 KB of LDS each), a few tokens per wavefront
-      const int64_t blocks = std::min<int64_t>((T_ + 3) / 4, 512);
-      launch_kernel(route_lds_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                    static_cast<const bf16_t*>(wg), bias, T_, d, K, idx, w, logits);
+      // two workgroups per CU (64 KB of LDS each), a few tokens per wavefront; two or four tokens
+      // per pass over W_g once there are enough tokens to fill the grid that way (router alone,
+      // us per call at T = 2048 / 4096 / 16384: one token 9.2 / 16.1 / 48.1, two 12.8 / 14.6 / 40.8,
+      // four 19.5 / 19.3 / 39.3)
+      const int tpw = T_ >= 16384 ? 4 : T_ >= 4096 ? 2 : 1;
+      const int64_t blocks = std::min<int64_t>((T_ + 4 * tpw - 1) / (4 * tpw), 512);
+      auto go = [&](auto k) {
+        launch_kernel(k, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                      static_cast<const bf16_t*>(wg), bias, T_, d, K, idx, w, logits);
+      };
+      if (tpw == 4) go(route_lds_kernel<4>);
+      else if (tpw == 2) go(route_lds_kernel<2>);
+      else go(route_lds_kernel<1>);
       return;
     }
   }

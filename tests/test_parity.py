@@ -148,6 +148,25 @@ def test_route(M, name):
     check_routing(w, gi, gw, gl, ol, oi, ow)
 
 
+# many-token router: one, two and four tokens per wavefront pass (T < 4096, < 16384, >= 16384), with
+# token counts that leave a ragged last pass
+MANY = {
+    "many_t2049": mi.Workload("many_t2049", T=2049, d=256, F=64, dtype="bf16", seed=621),
+    "many_t4097": mi.Workload("many_t4097", T=4097, d=512, F=64, dtype="bf16", seed=622),
+    "many_t16387": mi.Workload("many_t16387", T=16387, d=256, F=64, dtype="bf16", skew_bias=True, seed=623),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY))
+def test_route_many_tokens(M, name):
+    w = MANY[name]
+    say(f"[route] {name} T={w.T} d={w.d} E={w.E} K={w.K} {w.dtype}")
+    L = Layer(w)
+    gi, gw, gl = gpu_route(M, L)
+    ol, oi, ow = oracle.route(L.x, L.W["w_gate"], w.K, bias=L.W["bias"])
+    check_routing(w, gi, gw, gl, ol, oi, ow)
+
+
 @pytest.mark.parametrize("T,E,K,skew", [(1, 8, 2, 0.0), (1000, 8, 2, 0.0), (1000, 8, 2, 3.0), (4097, 8, 2, 1.0),
                                         (333, 16, 4, 2.0), (200, 64, 8, 0.0), (77, 1, 1, 0.0), (64, 8, 1, 5.0),
                                         (16384, 8, 2, 2.0)])
