@@ -67,9 +67,89 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// The same combine for K <= 2 and at most one k-range partial, with the slot count and the partial
+// count known at compile time: each thread loads four chunks' expert outputs (and partials, and y
+// when accumulating) before any arithmetic, instead of waiting out a memory round trip per chunk as
+// the generic loop does (its loads sit behind run-time slot and partial checks). Same arithmetic
+// in the same order as combine_kernel, so the results are bit-identical.
+template <int MODE, int TPB, int KT, int NP>
+__global__ __launch_bounds__(256) void combine_fast_kernel(const float* __restrict__ y_perm,
+                                                           const float* __restrict__ y_part,
+                                                           const int32_t* __restrict__ token_row,
+                                                           const float* __restrict__ topk_w, int64_t T, int d,
+                                                           void* __restrict__ y) {
+  constexpr int NT = 256 / TPB;  // threads per token
+  constexpr int U = 4;           // chunks of 4 columns loaded together
+  const int lt = threadIdx.x % NT;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / NT;
+  if (t >= T) return;
+  int64_t base[KT];
+  float g[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    base[k] = (int64_t)token_row[t * KT + k] * d;
+    g[k] = topk_w[t * KT + k];
+  }
+  for (int c0 = lt * 4; c0 < d; c0 += NT * 4 * U) {
+    f32x4_t o[U][KT], pp[U][NP > 0 ? KT : 1], yv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + NT * 4 * u;
+      const int cc = c < d ? c : c0;  // chunks past d load a valid chunk and are not stored
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        o[u][k] = *reinterpret_cast<const f32x4_t*>(y_perm + base[k] + cc);
+        if constexpr (NP > 0) pp[u][k] = *reinterpret_cast<const f32x4_t*>(y_part + base[k] + cc);
+      }
+      if constexpr (MODE == 2) yv[u] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(y) + t * d + cc);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + NT * 4 * u;
+      if (c >= d) continue;
+      f32x4_t e0 = o[u][0];
+      if constexpr (NP > 0) e0 = e0 + pp[u][0];
+      f32x4_t sum = g[0] * e0;
+#pragma unroll
+      for (int k = 1; k < KT; ++k) {
+        f32x4_t ek = o[u][k];
+        if constexpr (NP > 0) ek = ek + pp[u][k];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] = fmaf(g[k], ek[q], sum[q]);
+      }
+      if constexpr (MODE == 0) {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + t * d + c) = sum;
+      } else if constexpr (MODE == 1) {
+        *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(y) + t * d + c) =
+            u32x2_t{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+      } else {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + t * d + c) = yv[u] + sum;
+      }
+    }
+  }
+}
+
 template <int MODE>
 void launch_mode(const float* y_perm, const float* y_part, int nparts, const int32_t* token_row, const float* topk_w,
                  int64_t T, int d, int K, void* y, hipStream_t stream) {
+  if ((K == 1 || K == 2) && nparts <= 1) {
+    const unsigned blocks = (unsigned)(T <= 1024 ? T : (T + 3) / 4);
+    auto go = [&](auto kernel) {
+      launch_kernel(kernel, dim3(blocks), dim3(256), 0, stream, y_perm, y_part, token_row, topk_w, T, d, y);
+    };
+    if (T <= 1024) {
+      if (K == 2)
+        nparts ? go(combine_fast_kernel<MODE, 1, 2, 1>) : go(combine_fast_kernel<MODE, 1, 2, 0>);
+      else
+        nparts ? go(combine_fast_kernel<MODE, 1, 1, 1>) : go(combine_fast_kernel<MODE, 1, 1, 0>);
+    } else {
+      if (K == 2)
+        nparts ? go(combine_fast_kernel<MODE, 4, 2, 1>) : go(combine_fast_kernel<MODE, 4, 2, 0>);
+      else
+        nparts ? go(combine_fast_kernel<MODE, 4, 1, 1>) : go(combine_fast_kernel<MODE, 4, 1, 0>);
+    }
+    return;
+  }
   if (T <= 1024) {
     launch_kernel((combine_kernel<MODE, 1>), dim3((unsigned)T), dim3(256), 0, stream, y_perm, y_part, nparts,
                        token_row, topk_w, T, d, K, y);
