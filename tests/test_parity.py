@@ -169,7 +169,7 @@ def test_route_many_tokens(M, name):
 
 @pytest.mark.parametrize("T,E,K,skew", [(1, 8, 2, 0.0), (1000, 8, 2, 0.0), (1000, 8, 2, 3.0), (4097, 8, 2, 1.0),
                                         (333, 16, 4, 2.0), (200, 64, 8, 0.0), (77, 1, 1, 0.0), (64, 8, 1, 5.0),
-                                        (16384, 8, 2, 2.0)])
+                                        (16384, 8, 2, 2.0), (1025, 8, 2, 0.0), (3000, 4, 1, 1.0), (700, 8, 3, 0.5)])
 def test_permute(M, T, E, K, skew):
     say(f"[permute] T={T} E={E} K={K} skew={skew}")
     idx = mi.synthetic_routing(1000 + T + E, T, E, K, skew=skew)
