@@ -173,6 +173,67 @@ __global__ __launch_bounds__(256) void dx_kernel(const float* __restrict__ dxp, 
   }
 }
 
+// The same dx for E = 8, K <= 2 and at most one k-range partial, with K and the partial count known
+// at compile time: a column chunk's loads (the four W_g rows, every token's K rows of dxp and their
+// partials) are issued together before its arithmetic; the generic loop waits out a memory round trip
+// per load behind its run-time slot, partial and expert checks. Same arithmetic in the same order.
+template <int KT, int NP>
+__global__ __launch_bounds__(256) void dx_fast_kernel(const float* __restrict__ dxp, const float* __restrict__ part,
+                                                      const int32_t* __restrict__ token_row,
+                                                      const float* __restrict__ dlogits, const bf16_t* __restrict__ w_gate,
+                                                      int64_t T, int d, float* __restrict__ dx) {
+  const int64_t tb = (int64_t)blockIdx.x * kDxTokens;
+  const int nt = (int)min<int64_t>(kDxTokens, T - tb);
+  float dl[kDxTokens][8];
+  int64_t base[kDxTokens][KT];
+#pragma unroll
+  for (int i = 0; i < kDxTokens; ++i) {
+    const int64_t t = tb + (i < nt ? i : 0);  // tokens past the end read token tb and are not stored
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dl[i][e] = dlogits[t * 8 + e];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) base[i][k] = (int64_t)token_row[t * KT + k] * d;
+  }
+  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+    u32x4_t wr[4];
+    f32x4_t o[kDxTokens][KT], pp[kDxTokens][NP > 0 ? KT : 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wr[q] = load16(w_gate + (int64_t)(c + q) * 8);
+#pragma unroll
+    for (int i = 0; i < kDxTokens; ++i)
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        o[i][k] = *reinterpret_cast<const f32x4_t*>(dxp + base[i][k] + c);
+        if constexpr (NP > 0) pp[i][k] = *reinterpret_cast<const f32x4_t*>(part + base[i][k] + c);
+      }
+    float wg[4][8];  // W_g[c + q][e]
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wg[q][e] = (e & 1) ? bf16_hi(wr[q][e >> 1]) : bf16_lo(wr[q][e >> 1]);
+#pragma unroll
+    for (int i = 0; i < kDxTokens; ++i) {
+      if (i >= nt) break;
+      f32x4_t acc = o[i][0];
+      if constexpr (NP > 0) acc = acc + pp[i][0];
+#pragma unroll
+      for (int k = 1; k < KT; ++k) {
+        f32x4_t r = o[i][k];
+        if constexpr (NP > 0) r = r + pp[i][k];
+        acc = acc + r;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float rsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rsum = fmaf(wg[q][e], dl[i][e], rsum);
+        acc[q] += rsum;
+      }
+      *reinterpret_cast<f32x4_t*>(dx + (tb + i) * d + c) = acc;
+    }
+  }
+}
+
 // dW_g partials: chunk c of kDwgChunk tokens, part[c][j][e] = sum over its tokens t (ascending) of
 // x[t][j] * dlogit[t][e]. A thread takes C consecutive columns (4 with up to 8 experts: one 8-byte
 // load per token; 2 beyond) and its token loop is unrolled so that U loads are in flight; the
@@ -297,6 +358,17 @@ void launch_dx(const float* dxp, const float* part, int nparts, const int32_t* t
                const void* w_gate, int64_t T, int d, int E, int K, float* dx, hipStream_t s) {
   const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
   const int64_t stride = T * K * (int64_t)d;
+  const unsigned blocks = (unsigned)((T + kDxTokens - 1) / kDxTokens);
+  if (E == 8 && (K == 1 || K == 2) && nparts <= 1) {
+    auto go = [&](auto kernel) {
+      launch_kernel(kernel, dim3(blocks), dim3(256), 0, s, dxp, part, token_row, dlogits, wg, T, d, dx);
+    };
+    if (K == 2)
+      nparts ? go(dx_fast_kernel<2, 1>) : go(dx_fast_kernel<2, 0>);
+    else
+      nparts ? go(dx_fast_kernel<1, 1>) : go(dx_fast_kernel<1, 0>);
+    return;
+  }
   if (E <= 8)
     launch_kernel(dx_kernel<8>, dim3((unsigned)((T + kDxTokens - 1) / kDxTokens)), dim3(256), 0, s, dxp, part, nparts,
                   stride, token_row, dlogits, wg, T, d, E, K, dx);
