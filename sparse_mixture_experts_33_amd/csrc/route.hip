@@ -220,12 +220,7 @@ __global__ __launch_bounds__(256) void route_lds_kernel(const bf16_t* __restrict
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  // A token's x slices (lane l: k0 = 8 l + 512 i) are all loaded before its products, and the next
-  // token's while they run: a loop that waits for each slice before the next load pays a memory
-  // round trip per slice. Slices past d (and tokens past the end) load valid addresses; such slices
-  // are zeroed and read W_g's last slot, so they add exact zeros (the loads stay unconditional, which
-  // lets the compiler count them instead of waiting for all).
-  // TPW consecutive tokens per pass over W_g, so that each LDS read serves TPW tokens; a token's
+  // Lane l takes the x slices k0 = 8 l + 512 i of each token. TPW consecutive tokens per pass over W_g, so that each LDS read serves TPW tokens; a token's
   // products keep the order of the single-token pass (tokens past the end compute on the last one
   // and are not stored)
   for (int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * TPW; t0 < ntok;
